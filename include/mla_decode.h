@@ -1,0 +1,188 @@
+/*
+ * libmla_decode — MLA decode attention over a paged latent KV cache on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation (notation of "RFC: MsModeling 支持 Decode Context Parallel 仿真",
+ * §2.1.4 symbol table): B sequences, Q query tokens per sequence (Q = 1 plus
+ * speculative tokens), h_q query heads, one latent KV row per token shared by
+ * every head (h_kv = 1 for MLA) of D = kv_lora_rank + qk_rope_head_dim = 576
+ * bf16 columns, stored as [num_blocks, block_size, D] behind a block table
+ * (§2.1.4.1, table A).  For sequence b of length S_b, query token q sits at
+ * position pos = S_b - Q + q and attends a set A(b, q) of positions <= pos:
+ *
+ *   row(b, p) = block_table[b, p / block_size] * block_size + p % block_size
+ *   s_p       = scale * <q[b, q, h, 0:576], kv[row(b, p), 0:576]>
+ *   lse       = ln sum_{p in A} exp(s_p)                      (fp32)
+ *   out       = sum_{p in A} exp(s_p - lse) * kv[row(b, p), 0:512]
+ *
+ * V is the first d_v = 512 (kv_lora_rank) columns of the same latent row, and
+ * the output stays in that latent space (the up-projection is applied by the
+ * caller).  An empty A gives out = 0 and lse = -inf.  The attention op returns
+ * the fp32 lse next to the output as the DCP page's table B asks
+ * (§2.1.4.2, softmax_lse_flag).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device pointers; the library reads and
+ *    writes them only from kernels enqueued on `stream` (a hipStream_t; NULL
+ *    is the null stream).  The caller owns every buffer.  The library never
+ *    allocates, frees or synchronizes, keeps no state between calls, and is
+ *    safe to call from several host threads (calls on one stream run in order;
+ *    calls that share an output or workspace buffer on different streams race).
+ *  - Arrays are dense, row-major, with the shapes given below.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns its status and enqueues nothing (the failure rules of the
+ *    DCP page §2.1.3: illegal configurations are errors, raised before the
+ *    backend).  Device data (seq_lens, block_table, indices) is not inspected
+ *    on the host: positions outside [0, pos], and block-table entries outside
+ *    [0, num_blocks) for a position that is attended, are skipped on the device
+ *    instead of being read.  Callers must keep seq_lens[b] <= max_seq_len and
+ *    seq_lens[b] <= max_blocks * block_size.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  MLA_ERR_BAD_SHAPE = 2,           /* a size or stride is out of range */
+  MLA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (e.g. d_qk != 576) */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < mla_workspace_size(...) */
+  MLA_ERR_LAUNCH = 5,              /* the HIP runtime rejected a kernel launch */
+  MLA_ERR_DEVICE = 6               /* no usable gfx950 device for the current HIP device */
+} mla_status_t;
+
+typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
+
+/* Problem description shared by the decode calls. */
+typedef struct {
+  int32_t B;                  /* sequences, >= 1 */
+  int32_t Q;                  /* query tokens per sequence, 1..16; causal among them */
+  int32_t h_q;                /* query heads, 1..128 */
+  int32_t d_qk;               /* latent row width; must be 576 */
+  int32_t d_v;                /* value width (leading columns of the row); must be 512 */
+  float scale;                /* softmax scale applied to <q, k>, finite */
+  const void *q;              /* device, bf16 [B, Q, h_q, d_qk] (query already absorbed
+                                 into the latent space; RoPE part last) */
+  const void *kv;             /* device, bf16 [num_blocks, block_size, d_qk] */
+  int32_t num_blocks;         /* >= 1 */
+  int32_t block_size;         /* tokens per block, a power of two, 1..4096 */
+  const int32_t *block_table; /* device, int32 [B, max_blocks] physical block ids */
+  int32_t max_blocks;         /* >= 1 */
+  const int32_t *seq_lens;    /* device, int32 [B], each in [Q, max_seq_len] */
+  int32_t max_seq_len;        /* host-side upper bound on every seq_lens[b]; sizes the
+                                 split-KV plan, >= 1 and <= max_blocks * block_size */
+} mla_problem_t;
+
+/*
+ * Bytes of scratch the decode call needs for its split-KV partial results
+ * (fp32 partial outputs plus their lse).  `top_k` = 0 sizes a dense call,
+ * > 0 a sparse call with that list length; `num_shards`/`shard_id` as in
+ * mla_decode_dense.  Depends on the current HIP device's compute-unit count
+ * (256 is assumed when no device is visible).  Returns 0 when the plan needs
+ * no scratch, and (size_t)-1 when the arguments are invalid.
+ */
+size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards,
+                          int32_t shard_id, int32_t top_k);
+
+/*
+ * Dense decode: A(b, q) = { p : 0 <= p <= S_b - Q + q }.
+ *
+ * Decode context parallelism ("RFC: MsModeling 支持 Decode Context Parallel
+ * 仿真", §1.1 and §2.1.4.1): with num_shards = N > 1 the sequence is dealt to N
+ * shards in runs of `interleave` = I tokens, shard(p) = floor(p / I) mod N, and
+ * shard r attends only A(b, q) ∩ { p : shard(p) = r }.  Each shard emits a
+ * partial output plus lse in fp32 (the page upcasts both to fp32 before the
+ * exchange, §2.1.4.3); mla_merge_lse recombines them.
+ *
+ *  num_shards  >= 1.  1 = unsharded; `interleave` and `shard_id` are ignored.
+ *  interleave  >= 1 when num_shards > 1.
+ *  shard_id    -1 = compute every shard in this call; otherwise one shard in
+ *              [0, num_shards).
+ *  out         device.  Unsharded: [B, Q, h_q, d_v] in out_dtype.  Sharded:
+ *              fp32 [n_out, B, Q, h_q, d_v] with n_out = num_shards when
+ *              shard_id = -1, else 1 (out_dtype must be MLA_DTYPE_FP32).
+ *  lse         device, fp32 [B, Q, h_q] (unsharded) or [n_out, B, Q, h_q].
+ *  workspace   device scratch of workspace_bytes >= mla_workspace_size(problem,
+ *              num_shards, shard_id, 0); may be NULL when that size is 0.
+ */
+mla_status_t mla_decode_dense(const mla_problem_t *problem, int32_t num_shards,
+                              int32_t interleave, int32_t shard_id, void *out,
+                              mla_dtype_t out_dtype, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse (DSA/SFA) decode: each query token attends only the indexer-selected
+ * positions ("RFC: Context Parallel Modeling for DeepSeek-Style Attention"
+ * §3.6, bf16 sparse-attention inputs; the DCP page §1.3: the sparse path
+ * replaces S by top_k).  Entry (b, q, k), k < top_k, of `indices` is the
+ * logical token position at indices[b * index_stride_b + q * index_stride_q + k];
+ * A(b, q) is the multiset of entries i with 0 <= i <= S_b - Q + q, so -1
+ * padding (anywhere in the list) and out-of-range values are dropped and a
+ * repeated position counts as often as it appears.
+ *
+ *  indices         device, int32; the caller guarantees the strides stay inside it.
+ *  top_k           list length, 1..65536.
+ *  index_stride_b  elements between sequences, >= 0.
+ *  index_stride_q  elements between query tokens; 0 shares one list across Q.
+ *  out, lse        as the unsharded dense call.
+ *  workspace       >= mla_workspace_size(problem, 1, -1, top_k) bytes.
+ */
+mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indices,
+                               int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
+                               void *out, mla_dtype_t out_dtype, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * Online-softmax merge of n partial results ("RFC: MsModeling 支持 Decode
+ * Context Parallel 仿真", §1.1 and §2.1.4.3: after the exchange the partial
+ * outputs and lse are recombined locally).  For every row r:
+ *   M = max_i lse_i;  w_i = exp(lse_i - M);  lse = M + ln sum_i w_i;
+ *   out = sum_i w_i * o_i / sum_i w_i.
+ * Parts with lse = -inf carry no weight; a row whose parts are all -inf gives
+ * out = 0 and lse = -inf.
+ *
+ *  o_parts    device, fp32 [n, rows, d_v]
+ *  lse_parts  device, fp32 [n, rows]
+ *  n          1..1024;  rows >= 0;  d_v a multiple of 4 in 4..4096
+ *  out        device, [rows, d_v] in out_dtype;  lse_out device, fp32 [rows]
+ */
+mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t n,
+                           int64_t rows, int32_t d_v, void *out, mla_dtype_t out_dtype,
+                           float *lse_out, void *stream);
+
+/* Static, human-readable name of a status. */
+const char *mla_status_string(mla_status_t status);
+
+/*
+ * Host-only view of the split-KV plan a decode call would launch (no device
+ * access).  `num_cus` stands in for the device's compute-unit count.
+ * Returns MLA_OK and fills *plan, or the status the decode call would return
+ * for these arguments.
+ */
+typedef struct {
+  int32_t q_per_group;    /* query tokens handled together by one work-group */
+  int32_t rows_per_group; /* q_per_group * h_q */
+  int32_t units;          /* (sequence, query group, shard) work units */
+  int32_t splits;         /* KV partitions per unit */
+  int32_t chunk;          /* tokens per partition (multiple of the 64-token tile) */
+  int32_t stream_len;     /* longest per-unit token stream the plan covers */
+  int64_t grid;           /* work-groups in the decode launch = units * splits */
+  size_t workspace_bytes; /* scratch the plan needs */
+} mla_plan_t;
+
+mla_status_t mla_plan_query(const mla_problem_t *problem, int32_t num_shards,
+                            int32_t interleave, int32_t shard_id, int32_t top_k,
+                            int64_t index_stride_q, int32_t num_cus, mla_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,295 @@
+// Host side of libmla_decode: argument checks, the split-KV planner and the
+// C-ABI entry points declared in include/mla_decode.h.
+//
+// The planner sizes one launch to the device: a work-group per compute unit
+// (each work-group holds two 72 KiB LDS tiles, so one fits per CU).  When the
+// natural units (sequence x query group x shard) are fewer than the CUs, each
+// unit's token stream is cut into `splits` partitions of whole 64-token tiles;
+// the partitions write fp32 partial (O, lse) pairs to the caller's workspace
+// and the merge kernel combines them with the same log-sum-exp rule as the
+// DCP exchange ("RFC: MsModeling 支持 Decode Context Parallel 仿真", §1.1,
+// §2.1.4.3).
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/mla_decode.h"
+#include "mla_internal.h"
+
+namespace {
+
+using namespace mla;
+
+constexpr int kDefaultCus = 256;  // MI355X
+constexpr int kMaxShards = 4096;
+constexpr int kMaxTopK = 65536;
+constexpr int kMaxMergeParts = 1024;
+
+struct Plan {
+  int q_per_group, rows_per_group, q_groups, shard_units;
+  int units, splits, chunk, stream_len;
+  int64_t grid;
+  size_t ws_o, ws_lse, ws_total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t shard_len_host(int64_t S, int64_t N, int64_t I, int64_t r) {
+  if (S <= 0) return 0;
+  const int64_t full = S / I, rem = S % I;
+  const int64_t groups = full > r ? (full - 1 - r) / N + 1 : 0;
+  return groups * I + ((full % N) == r ? rem : 0);
+}
+
+mla_status_t check_problem(const mla_problem_t *p) {
+  if (!p) return MLA_ERR_NULL_POINTER;
+  if (!p->q || !p->kv || !p->block_table || !p->seq_lens) return MLA_ERR_NULL_POINTER;
+  if (p->d_qk != kDqk || p->d_v != kDv) return MLA_ERR_UNSUPPORTED;
+  if (p->B < 1 || p->Q < 1 || p->h_q < 1 || p->num_blocks < 1 || p->max_blocks < 1 ||
+      p->max_seq_len < 1)
+    return MLA_ERR_BAD_SHAPE;
+  if (p->Q > 16 || p->h_q > kMaxRowsPerGroup) return MLA_ERR_UNSUPPORTED;
+  if (p->block_size < 1 || p->block_size > 4096 || (p->block_size & (p->block_size - 1)))
+    return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)p->num_blocks * p->block_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)p->max_seq_len > (int64_t)p->max_blocks * p->block_size) return MLA_ERR_BAD_SHAPE;
+  if (p->max_seq_len < p->Q) return MLA_ERR_BAD_SHAPE;
+  if (!std::isfinite(p->scale)) return MLA_ERR_BAD_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(p->q) | reinterpret_cast<uintptr_t>(p->kv)) & 15)
+    return MLA_ERR_BAD_SHAPE;  // rows are moved in 16-byte pieces
+  return MLA_OK;
+}
+
+mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, int shard_id,
+                       int top_k, int64_t idx_stride_q, int num_cus, Plan *pl) {
+  const bool sparse = top_k > 0;
+  if (top_k < 0 || top_k > kMaxTopK) return MLA_ERR_BAD_SHAPE;
+  if (num_shards < 1 || num_shards > kMaxShards) return MLA_ERR_BAD_SHAPE;
+  if (num_shards > 1) {
+    if (sparse) return MLA_ERR_UNSUPPORTED;
+    if (interleave < 1 || shard_id < -1 || shard_id >= num_shards) return MLA_ERR_BAD_SHAPE;
+  }
+  if (num_cus < 1) num_cus = kDefaultCus;
+  const int rows_all = p->Q * p->h_q;
+  const bool shared_list = !sparse || idx_stride_q == 0 || p->Q == 1;
+  pl->q_per_group =
+      (shared_list && rows_all <= kMaxRowsPerGroup && p->Q <= kMaxQPerGroup) ? p->Q : 1;
+  pl->rows_per_group = pl->q_per_group * p->h_q;
+  pl->q_groups = p->Q / pl->q_per_group;
+  pl->shard_units = (num_shards > 1 && shard_id < 0) ? num_shards : 1;
+  int64_t L;
+  if (sparse) {
+    L = top_k;
+  } else if (num_shards > 1) {
+    L = 0;
+    const int r0 = shard_id < 0 ? 0 : shard_id, r1 = shard_id < 0 ? num_shards : shard_id + 1;
+    for (int r = r0; r < r1; ++r)
+      L = std::max<int64_t>(L, shard_len_host(p->max_seq_len, num_shards, interleave, r));
+  } else {
+    L = p->max_seq_len;
+  }
+  pl->stream_len = (int)L;
+  const int64_t units = (int64_t)p->B * pl->q_groups * pl->shard_units;
+  if (units > INT32_MAX) return MLA_ERR_BAD_SHAPE;
+  pl->units = (int)units;
+  const int64_t tiles = (L + kTile - 1) / kTile;
+  int64_t splits = 1;
+  if (units < num_cus && tiles > 1) splits = std::min<int64_t>((num_cus + units - 1) / units, tiles);
+  const int64_t tiles_per_split = tiles > 0 ? (tiles + splits - 1) / splits : 1;
+  splits = tiles > 0 ? (tiles + tiles_per_split - 1) / tiles_per_split : 1;
+  pl->splits = (int)splits;
+  pl->chunk = (int)(tiles_per_split * kTile);
+  pl->grid = units * splits;
+  if (pl->grid > INT32_MAX) return MLA_ERR_BAD_SHAPE;
+  const int64_t rows_total = (int64_t)p->B * p->Q * p->h_q;
+  if (splits > 1) {
+    const int64_t parts = (int64_t)pl->shard_units * splits;
+    pl->ws_o = align256((size_t)(parts * rows_total * kDv) * sizeof(float));
+    pl->ws_lse = align256((size_t)(parts * rows_total) * sizeof(float));
+  } else {
+    pl->ws_o = pl->ws_lse = 0;
+  }
+  pl->ws_total = pl->ws_o + pl->ws_lse;
+  return MLA_OK;
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kDefaultCus;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return kDefaultCus;
+  return n;
+}
+
+mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int32_t *indices,
+                 int top_k, int64_t stride_b, int64_t stride_q, int num_shards, int interleave,
+                 int shard_id, void *out, bool out_fp32, float *lse, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+  if (pl.ws_total > 0) {
+    if (!workspace) return MLA_ERR_NULL_POINTER;
+    if (workspace_bytes < pl.ws_total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_BAD_SHAPE;
+  }
+  if (reinterpret_cast<uintptr_t>(out) & 15) return MLA_ERR_BAD_SHAPE;
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t *>(p->q);
+  a.kv = static_cast<const uint16_t *>(p->kv);
+  a.block_table = p->block_table;
+  a.seq_lens = p->seq_lens;
+  a.indices = indices;
+  a.idx_stride_b = stride_b;
+  a.idx_stride_q = stride_q;
+  a.top_k = top_k;
+  a.sparse = sparse ? 1 : 0;
+  a.B = p->B;
+  a.Q = p->Q;
+  a.h_q = p->h_q;
+  a.block_size = p->block_size;
+  a.bs_shift = 0;
+  while ((1 << a.bs_shift) < p->block_size) ++a.bs_shift;
+  a.max_blocks = p->max_blocks;
+  a.num_blocks = p->num_blocks;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a.num_shards = num_shards;
+  a.interleave = num_shards > 1 ? interleave : 1;
+  a.shard_base = (num_shards > 1 && shard_id >= 0) ? shard_id : 0;
+  a.shard_units = pl.shard_units;
+  a.q_per_group = pl.q_per_group;
+  a.rows_per_group = pl.rows_per_group;
+  a.q_groups = pl.q_groups;
+  a.splits = pl.splits;
+  a.chunk = pl.chunk;
+  a.rows_total = (int64_t)p->B * p->Q * p->h_q;
+  a.out = out;
+  a.out_fp32 = out_fp32 ? 1 : 0;
+  a.lse = lse;
+  if (pl.splits > 1) {
+    a.part_o = static_cast<float *>(workspace);
+    a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_o);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_decode(a, pl.grid, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (pl.splits > 1) {
+    MergeArgs m;
+    m.o_parts = a.part_o;
+    m.lse_parts = a.part_lse;
+    m.n = pl.splits;
+    m.rows = a.rows_total;
+    m.d_v = kDv;
+    m.groups = pl.shard_units;
+    m.out = out;
+    m.out_fp32 = a.out_fp32;
+    m.lse_out = lse;
+    if (launch_merge(m, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards, int32_t shard_id,
+                          int32_t top_k) {
+  if (check_problem(problem) != MLA_OK) return (size_t)-1;
+  Plan pl;
+  // A shared index list never plans fewer partitions than per-token lists, so
+  // its size covers both.
+  if (make_plan(problem, num_shards, 1, shard_id, top_k, 0, device_cus(), &pl) != MLA_OK)
+    return (size_t)-1;
+  return pl.ws_total;
+}
+
+mla_status_t mla_decode_dense(const mla_problem_t *problem, int32_t num_shards,
+                              int32_t interleave, int32_t shard_id, void *out,
+                              mla_dtype_t out_dtype, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  mla_status_t st = check_problem(problem);
+  if (st != MLA_OK) return st;
+  if (!out || !lse) return MLA_ERR_NULL_POINTER;
+  if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_BAD_SHAPE;
+  if (num_shards > 1 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_UNSUPPORTED;
+  Plan pl;
+  st = make_plan(problem, num_shards, interleave, shard_id, 0, 0, device_cus(), &pl);
+  if (st != MLA_OK) return st;
+  return run(problem, pl, false, nullptr, 0, 0, 0, num_shards, interleave, shard_id, out,
+             out_dtype == MLA_DTYPE_FP32, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indices,
+                               int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
+                               void *out, mla_dtype_t out_dtype, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  mla_status_t st = check_problem(problem);
+  if (st != MLA_OK) return st;
+  if (!indices || !out || !lse) return MLA_ERR_NULL_POINTER;
+  if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_BAD_SHAPE;
+  if (top_k < 1 || index_stride_b < 0 || index_stride_q < 0) return MLA_ERR_BAD_SHAPE;
+  Plan pl;
+  st = make_plan(problem, 1, 1, -1, top_k, index_stride_q, device_cus(), &pl);
+  if (st != MLA_OK) return st;
+  return run(problem, pl, true, indices, top_k, index_stride_b, index_stride_q, 1, 1, -1, out,
+             out_dtype == MLA_DTYPE_FP32, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t n,
+                           int64_t rows, int32_t d_v, void *out, mla_dtype_t out_dtype,
+                           float *lse_out, void *stream) {
+  if (!o_parts || !lse_parts || !out || !lse_out) return MLA_ERR_NULL_POINTER;
+  if (n < 1 || n > kMaxMergeParts || rows < 0 || rows > INT32_MAX || d_v < 4 || d_v > 4096 ||
+      (d_v & 3))
+    return MLA_ERR_BAD_SHAPE;
+  if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_BAD_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(o_parts) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return MLA_ERR_BAD_SHAPE;
+  if (rows == 0) return MLA_OK;
+  MergeArgs m;
+  m.o_parts = o_parts;
+  m.lse_parts = lse_parts;
+  m.n = n;
+  m.rows = rows;
+  m.d_v = d_v;
+  m.groups = 1;
+  m.out = out;
+  m.out_fp32 = out_dtype == MLA_DTYPE_FP32 ? 1 : 0;
+  m.lse_out = lse_out;
+  if (launch_merge(m, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+const char *mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER: a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE: a size, stride or alignment is out of range";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: valid arguments this library does not implement";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < mla_workspace_size()";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable gfx950 device";
+  }
+  return "unknown mla_status_t";
+}
+
+mla_status_t mla_plan_query(const mla_problem_t *problem, int32_t num_shards, int32_t interleave,
+                            int32_t shard_id, int32_t top_k, int64_t index_stride_q,
+                            int32_t num_cus, mla_plan_t *plan) {
+  mla_status_t st = check_problem(problem);
+  if (st != MLA_OK) return st;
+  if (!plan) return MLA_ERR_NULL_POINTER;
+  Plan pl;
+  st = make_plan(problem, num_shards, interleave, shard_id, top_k, index_stride_q, num_cus, &pl);
+  if (st != MLA_OK) return st;
+  plan->q_per_group = pl.q_per_group;
+  plan->rows_per_group = pl.rows_per_group;
+  plan->units = pl.units;
+  plan->splits = pl.splits;
+  plan->chunk = pl.chunk;
+  plan->stream_len = pl.stream_len;
+  plan->grid = pl.grid;
+  plan->workspace_bytes = pl.ws_total;
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the host-side planner (mla_api.cpp) and the
+// device kernels (mla_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mla {
+
+constexpr int kDqk = 576;        // latent row width: kv_lora_rank 512 + RoPE 64
+constexpr int kDv = 512;         // value columns = leading kv_lora_rank columns
+constexpr int kTile = 64;        // tokens staged in LDS per pipeline step
+constexpr int kMaxRowsPerGroup = 128;  // query rows (q token x head) per work-group
+constexpr int kMaxQPerGroup = 4;       // query tokens per work-group (attended masks kept per token)
+
+// Everything one decode launch needs.  Passed by value as the kernel argument.
+struct DecodeArgs {
+  const uint16_t *q;           // bf16 [B, Q, h_q, 576]
+  const uint16_t *kv;          // bf16 [num_blocks, block_size, 576]
+  const int32_t *block_table;  // [B, max_blocks]
+  const int32_t *seq_lens;     // [B]
+  const int32_t *indices;      // sparse only
+  int64_t idx_stride_b, idx_stride_q;
+  int32_t top_k;
+  int32_t sparse;
+  int32_t B, Q, h_q;
+  int32_t block_size, bs_shift, max_blocks, num_blocks;
+  float scale_log2;            // scale * log2(e): scores are kept in base-2 units
+  int32_t num_shards, interleave, shard_base, shard_units;
+  int32_t q_per_group, rows_per_group, q_groups;
+  int32_t splits, chunk;
+  int64_t rows_total;          // B * Q * h_q
+  // final results (splits == 1)
+  void *out;
+  int32_t out_fp32;
+  float *lse;
+  // split-KV partial results (splits > 1): [shard_units * splits, rows_total, 512] and lse
+  float *part_o;
+  float *part_lse;
+};
+
+struct MergeArgs {
+  const float *o_parts;   // [groups * n, rows, d_v]
+  const float *lse_parts; // [groups * n, rows]
+  int32_t n;
+  int64_t rows;
+  int32_t d_v;
+  int32_t groups;
+  void *out;              // [groups, rows, d_v]
+  int32_t out_fp32;
+  float *lse_out;         // [groups, rows]
+};
+
+// Enqueue the kernels; return the HIP status of the launch.
+hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs &args, hipStream_t stream);
+
+}  // namespace mla

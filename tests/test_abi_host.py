@@ -1,0 +1,138 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header
+declares, rejects bad arguments before touching the device, and plans split-KV
+partitions that cover every token exactly once."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+md = pytest.importorskip("latent_decode_attention_amd.mla_decode",
+                         reason="libmla_decode.so not built (run __graft_entry__.build())")
+lib = md.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("mla_decode_dense", "mla_decode_sparse", "mla_merge_lse", "mla_workspace_size",
+                 "mla_status_string", "mla_plan_query"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in md.STATUS_NAMES.items():
+        assert md.mla_status_string(code).startswith(name)
+    assert "unknown" in md.mla_status_string(99)
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def problem(**kw):
+    base = dict(B=2, Q=1, h_q=128, d_qk=576, d_v=512, scale=0.07, q=FAKE, kv=FAKE, num_blocks=64,
+                block_size=64, block_table=FAKE, max_blocks=32, seq_lens=FAKE, max_seq_len=2048)
+    base.update(kw)
+    return md.Problem(**base)
+
+
+def dense_status(p, num_shards=1, interleave=1, shard_id=-1, out=FAKE, dtype=0, lse=FAKE):
+    return lib.mla_decode_dense(ctypes.byref(p) if p is not None else None, num_shards, interleave,
+                                shard_id, out, dtype, lse, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(block_table=None), 1), (dict(seq_lens=None), 1),
+    (dict(d_qk=512), 3), (dict(d_v=576), 3), (dict(h_q=129), 3), (dict(Q=17), 3),
+    (dict(B=0), 2), (dict(h_q=0), 2), (dict(block_size=48), 2), (dict(block_size=0), 2),
+    (dict(max_seq_len=2049 + 31 * 64), 2), (dict(max_seq_len=0), 2), (dict(scale=float("nan")), 2),
+    (dict(q=FAKE + 8), 2),
+])
+def test_dense_validation_statuses(kw, status):
+    assert dense_status(problem(**kw)) == status
+
+
+def test_dense_argument_statuses():
+    assert dense_status(None) == 1
+    assert dense_status(problem(), out=None) == 1
+    assert dense_status(problem(), lse=None) == 1
+    assert dense_status(problem(), dtype=7) == 2
+    assert dense_status(problem(), num_shards=0) == 2
+    assert dense_status(problem(), num_shards=4, interleave=0, dtype=1) == 2
+    assert dense_status(problem(), num_shards=4, interleave=8, shard_id=4, dtype=1) == 2
+    # sharded partials are fp32 only
+    assert dense_status(problem(), num_shards=4, interleave=8, dtype=0) == 3
+    # a plan that needs scratch without a workspace
+    assert dense_status(problem()) == 1
+
+
+def test_sparse_and_merge_argument_statuses():
+    p = problem()
+    f = lib.mla_decode_sparse
+    assert f(ctypes.byref(p), None, 2048, 2048, 0, FAKE, 0, FAKE, None, 0, None) == 1
+    assert f(ctypes.byref(p), FAKE, 0, 2048, 0, FAKE, 0, FAKE, None, 0, None) == 2
+    assert f(ctypes.byref(p), FAKE, 2048, -1, 0, FAKE, 0, FAKE, None, 0, None) == 2
+    assert f(ctypes.byref(p), FAKE, 70000, 70000, 0, FAKE, 0, FAKE, None, 0, None) == 2
+    assert f(ctypes.byref(p), FAKE, 2048, 2048, 0, FAKE, 0, FAKE, FAKE, 16, None) == 4
+    m = lib.mla_merge_lse
+    assert m(None, FAKE, 2, 4, 512, FAKE, 1, FAKE, None) == 1
+    assert m(FAKE, FAKE, 0, 4, 512, FAKE, 1, FAKE, None) == 2
+    assert m(FAKE, FAKE, 2, 4, 510, FAKE, 1, FAKE, None) == 2
+    assert m(FAKE, FAKE, 2, -1, 512, FAKE, 1, FAKE, None) == 2
+    assert m(FAKE, FAKE, 2, 0, 512, FAKE, 1, FAKE, None) == 0  # nothing to do
+
+
+def plan(p, **kw):
+    return md.mla_plan_query(p, **kw)
+
+
+def test_plan_fills_the_device_and_covers_every_tile():
+    # sparse B=32 h=128 top_k=2048: 32 units -> 8 partitions of 256 tokens
+    pl = plan(problem(B=32, max_seq_len=32768, max_blocks=512), top_k=2048)
+    assert (pl["units"], pl["splits"], pl["chunk"], pl["grid"]) == (32, 8, 256, 256)
+    assert pl["workspace_bytes"] >= 8 * 32 * 128 * 512 * 4
+    # dense B=32 S=4096
+    pl = plan(problem(B=32, max_seq_len=4096, max_blocks=64))
+    assert (pl["splits"], pl["chunk"], pl["grid"]) == (8, 512, 256)
+    # enough units: no partitions, no scratch
+    pl = plan(problem(B=512, max_seq_len=4096, max_blocks=64))
+    assert pl["splits"] == 1 and pl["workspace_bytes"] == 0
+    # MTP: Q=2 x h=64 share one work-group
+    pl = plan(problem(B=128, Q=2, h_q=64, max_seq_len=65536, max_blocks=1024), top_k=2048)
+    assert pl["q_per_group"] == 2 and pl["rows_per_group"] == 128 and pl["units"] == 128
+    # per-token index lists split the query tokens
+    pl = plan(problem(B=128, Q=2, h_q=64, max_seq_len=65536, max_blocks=1024), top_k=2048,
+              index_stride_q=2048)
+    assert pl["q_per_group"] == 1 and pl["units"] == 256
+
+
+@pytest.mark.parametrize("S,N,I", [(131072, 8, 64), (1000, 3, 7), (5, 8, 64), (64 * 8 * 3 + 17, 8, 64)])
+def test_plan_shards_cover_their_positions(S, N, I):
+    for r in list(range(N)) + [-1]:
+        pl = plan(problem(B=8, max_seq_len=S, max_blocks=(S + 63) // 64), num_shards=N, interleave=I,
+                  shard_id=r)
+        counts = [sum(1 for p in range(S) if (p // I) % N == rr) for rr in range(N)]
+        want = max(counts) if r < 0 else counts[r]
+        assert pl["stream_len"] == want
+        assert pl["splits"] * pl["chunk"] >= want and pl["chunk"] % 64 == 0
+        assert (pl["splits"] - 1) * pl["chunk"] < max(want, 1)
+        units = 8 * (N if r < 0 else 1)
+        assert pl["grid"] == units * pl["splits"]
+
+
+def test_plan_rejects_sparse_shards():
+    assert lib.mla_plan_query(ctypes.byref(problem()), 2, 64, -1, 2048, 0, 256,
+                              ctypes.byref(md.Plan())) == 3

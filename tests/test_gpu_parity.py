@@ -1,0 +1,359 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (fp32 accumulation, scores exact up to fp32 summation):
+  * lse: |Δ| <= 1e-3;
+  * O in fp32: |Δ| <= 1e-2;
+  * O in bf16: |Δ| <= 1e-2 + half a bf16 ulp at |O_ref| + 1e-2.  The result is
+    computed in fp32 (held to 1e-2 by the fp32 runs) and then rounded to
+    nearest bf16, which by itself moves it by up to half an ulp: 0.0078 at
+    |O| in [2, 4), more than 1e-2 beyond 4.
+Index and gather semantics (which positions are attended, -1 padding, block-table
+mapping) are checked exactly with one-hot probes and bitwise invariances.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from helpers import bf16, f64, random_rows, workload  # noqa: E402
+from latent_decode_attention_amd import mla_decode as md  # noqa: E402
+from latent_decode_attention_amd import workloads as W  # noqa: E402
+from latent_decode_attention_amd.device import upload, run  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def ulp_bf16(x):
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def assert_o_close(o_gpu, o_ref, what=""):
+    g = o_gpu.float().cpu().numpy().astype(np.float64).reshape(o_ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - o_ref)
+    if o_gpu.dtype == torch.bfloat16:
+        tol = 1e-2 + 0.5 * ulp_bf16(np.abs(o_ref) + 1e-2)
+    else:
+        tol = np.full_like(o_ref, 1e-2)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.3g}"
+    return float(err.max())
+
+
+def assert_lse_close(l_gpu, l_ref, what=""):
+    g = l_gpu.float().cpu().numpy().astype(np.float64).reshape(l_ref.shape)
+    both_inf = np.isneginf(g) & np.isneginf(l_ref)
+    err = np.where(both_inf, 0.0, np.abs(g - l_ref))
+    assert np.all(err <= 1e-3), f"{what}: lse max err {np.nanmax(err):.3g}"
+    return float(err.max())
+
+
+def oracle_of(w, rows=None, shard=None):
+    if w.indices is not None:
+        return oracle.sparse(w, rows=rows)
+    if shard is not None:
+        return oracle.dense(w, rows=rows, num_shards=w.num_shards, interleave=w.interleave, shard_id=shard)
+    return oracle.dense(w, rows=rows)
+
+
+def check_full(w, out_dtype=torch.bfloat16):
+    d = upload(w)
+    out, lse = run(d, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle_of(w)
+    assert_o_close(out, ro, w.name)
+    assert_lse_close(lse, rl, w.name)
+    return out, lse
+
+
+# ---------------------------------------------------------------- full compares
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tiny_dense_config(out_dtype):
+    check_full(W.config_tiny(), out_dtype)
+
+
+@pytest.mark.parametrize("h_q,Q", [(128, 1), (64, 2), (16, 1), (32, 3), (128, 2)])
+def test_dense_ragged_paged(h_q, Q):
+    w = W.make_workload("dense_ragged", 3, Q, h_q, [1000, 77, 300], 16, seed=7 + h_q + Q)
+    check_full(w)
+
+
+def test_dense_block_size_64_long():
+    w = W.make_workload("dense_long", 2, 1, 128, [2048 + 64 * 7 + 5, 513], 64, seed=21)
+    check_full(w, torch.float32)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_sparse_small(shared):
+    w = W.make_workload("sparse_small", 4, 2, 64, [5000, 300, 2049, 64], 64, seed=31, top_k=256,
+                        shared_q_indices=shared, short_rows=1, short_valid=100)
+    check_full(w)
+
+
+def test_sparse_out_of_range_duplicates_and_causal_limit():
+    w = W.make_workload("sparse_edge", 2, 2, 128, [700, 130], 16, seed=41, top_k=200)
+    idx = w.indices.reshape(2, 200).copy()
+    idx[0, :6] = [699, 698, 5, 5, 100000, -7]    # 699 only for q=1; duplicate 5; out of range
+    idx[1, 10:20] = -1                           # padding in the middle
+    w.indices = idx.reshape(-1).astype(np.int32)
+    check_full(w, torch.float32)
+
+
+def test_sharded_then_merge_equals_unsharded():
+    w = W.make_workload("sharded", 2, 1, 128, [3000, 1111], 16, seed=51, num_shards=3, interleave=16)
+    d = upload(w)
+    parts, lses = run(d)
+    torch.cuda.synchronize()
+    for r in range(3):
+        ro, rl = oracle.dense(w, num_shards=3, interleave=16, shard_id=r)
+        assert_o_close(parts[r], ro, f"shard {r}")
+        assert_lse_close(lses[r], rl, f"shard {r}")
+    # one shard at a time gives the same bytes as the all-shards call
+    one, one_l = md.mla_decode_dense(d.q, d.kv, d.block_table, d.seq_lens, scale=w.scale,
+                                     max_seq_len=w.max_seq_len, num_shards=3, interleave=16, shard_id=1)
+    assert torch.equal(one[0], parts[1]) and torch.equal(one_l[0], lses[1])
+    merged, mlse = md.mla_merge_lse(parts.contiguous(), lses.contiguous(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.dense(w)
+    assert_o_close(merged, ro, "merged")
+    assert_lse_close(mlse, rl, "merged")
+
+
+def test_merge_kernel_against_oracle():
+    g = np.random.default_rng(3)
+    n, rows = 5, 300
+    o = g.standard_normal((n, rows, 512)).astype(np.float32)
+    l = (g.standard_normal((n, rows)) * 4).astype(np.float32)
+    l[1, :50] = -np.inf
+    l[:, 60] = -np.inf
+    ro, rl = oracle.merge(o.astype(np.float64), l.astype(np.float64))
+    for dt in (torch.float32, torch.bfloat16):
+        out, lse = md.mla_merge_lse(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), out_dtype=dt)
+        torch.cuda.synchronize()
+        assert_o_close(out, ro, "merge")
+        assert_lse_close(lse, rl, "merge")
+    assert torch.all(out[60].float() == 0) and torch.isneginf(lse[60])
+
+
+# ---------------------------------------------------------------- exact probes
+
+def one_hot_workload(S, Q, block_size, seed, **kw):
+    rows = np.zeros((S, W.D_QK), dtype=np.uint16)
+    rows[np.arange(S), np.arange(S)] = bf16(1.0)
+    q = np.zeros((1, Q, 32, W.D_QK), dtype=np.uint16)   # every score 0: uniform weights
+    return workload(q, [rows], block_size=block_size, seed=seed, spare=3, **kw)
+
+
+def attended_sets(out, lse, Q):
+    o = out.float().cpu().numpy().reshape(Q, 32, 512)
+    l = lse.cpu().numpy().reshape(Q, 32)
+    sets = []
+    for qi in range(Q):
+        cols = [set(np.nonzero(o[qi, h] != 0)[0].tolist()) for h in range(32)]
+        assert all(c == cols[0] for c in cols)
+        A = cols[0]
+        if A:
+            np.testing.assert_allclose(o[qi, 0, sorted(A)], 1.0 / len(A), rtol=1e-6)
+            assert abs(l[qi, 0] - math.log(len(A))) < 1e-5
+        else:
+            assert np.isneginf(l[qi]).all()
+        sets.append(A)
+    return sets
+
+
+@pytest.mark.parametrize("S,Q,N,I", [(500, 2, 1, 1), (300, 1, 3, 8), (511, 3, 4, 64), (97, 2, 8, 16)])
+def test_one_hot_probe_dense_and_shards(S, Q, N, I):
+    w = one_hot_workload(S, Q, 16, seed=S)
+    d = upload(w)
+    if N == 1:
+        out, lse = md.mla_decode_dense(d.q, d.kv, d.block_table, d.seq_lens, scale=w.scale,
+                                       max_seq_len=w.max_seq_len, out_dtype=torch.float32)
+        got = attended_sets(out, lse, Q)
+        for qi in range(Q):
+            assert got[qi] == set(range(S - Q + qi + 1))
+    else:
+        outs, lses = md.mla_decode_dense(d.q, d.kv, d.block_table, d.seq_lens, scale=w.scale,
+                                         max_seq_len=w.max_seq_len, num_shards=N, interleave=I)
+        for r in range(N):
+            got = attended_sets(outs[r], lses[r], Q)
+            for qi in range(Q):
+                assert got[qi] == {p for p in range(S - Q + qi + 1) if (p // I) % N == r}
+
+
+def test_one_hot_probe_sparse_padding_duplicates():
+    S, Q = 400, 2
+    idx = np.full(300, -1, dtype=np.int32)
+    sel = np.random.default_rng(5).choice(S, 250, replace=False)
+    idx[:250] = sel
+    idx[250:255] = [S - 1, S - 1, 7, 100000, -3]    # S-1 only visible to q=1; 7 maybe duplicate
+    w = one_hot_workload(S, Q, 16, seed=9, indices=idx, top_k=300, index_stride_b=300, index_stride_q=0)
+    d = upload(w)
+    out, lse = run(d, out_dtype=torch.float32)
+    o = out.float().cpu().numpy().reshape(Q, 32, 512)
+    for qi in range(Q):
+        last = S - Q + qi
+        valid = [int(i) for i in idx if 0 <= i <= last]
+        counts = np.bincount(valid, minlength=512) / len(valid)
+        np.testing.assert_allclose(o[qi, 5], counts, rtol=1e-6, atol=0)
+        assert abs(lse.cpu().numpy().reshape(Q, 32)[qi, 5] - math.log(len(valid))) < 1e-5
+
+
+def test_nan_poison_in_unreferenced_rows_never_reaches_output():
+    w = W.make_workload("poison", 2, 2, 64, [900, 2000], 64, seed=61, top_k=333)
+    ref = oracle.sparse(w)
+    # poison every cache row that no list entry selects (and the spare blocks already are)
+    keep = np.zeros(w.kv.shape[:2], dtype=bool)
+    for b in range(2):
+        for i in w.indices.reshape(2, -1)[b]:
+            if 0 <= i < w.seq_lens[b]:
+                blk = w.block_table[b, i // 64]
+                keep[blk, i % 64] = True
+    w.kv[~keep] = W.BF16_NAN
+    out, lse = run(upload(w), out_dtype=torch.float32)
+    assert_o_close(out, ref[0], "poisoned")
+    assert_lse_close(lse, ref[1], "poisoned")
+
+
+def test_block_table_permutation_is_bitwise_invisible():
+    rng = np.random.default_rng(71)
+    logical = [random_rows(rng, 1500), random_rows(rng, 333)]
+    q = random_rows(rng, 2 * 128).reshape(2, 1, 128, W.D_QK)
+    a = run(upload(workload(q, logical, block_size=16, seed=1)))
+    b = run(upload(workload(q, logical, block_size=16, seed=2, spare=9)))
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_padding_and_out_of_range_entries_are_bitwise_equivalent():
+    w = W.make_workload("pad", 3, 1, 128, [32768] * 3, 64, seed=81, top_k=2048, short_rows=3,
+                        short_valid=1500)
+    d = upload(w)
+    a = run(d)
+    idx = w.indices.copy().reshape(3, 2048)
+    idx[:, 1500:] = 1 << 30           # beyond every causal limit instead of -1
+    b = run(d, indices=torch.from_numpy(idx.reshape(-1)).cuda())
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # and the compact list gives the same result up to rounding (different tiling)
+    compact = np.ascontiguousarray(idx[:, :1500])
+    c = md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, torch.from_numpy(compact).cuda(),
+                             scale=w.scale, max_seq_len=w.max_seq_len, out_dtype=torch.float32)
+    ro, rl = oracle.sparse(w)
+    assert_o_close(c[0], ro, "compact")
+    assert_lse_close(c[1], rl, "compact")
+
+
+def test_causal_first_token_equals_shorter_single_token_call_bitwise():
+    rng = np.random.default_rng(91)
+    logical = [random_rows(rng, 2000), random_rows(rng, 700)]
+    q2 = random_rows(rng, 2 * 2 * 64).reshape(2, 2, 64, W.D_QK)
+    w2 = workload(q2, logical, block_size=16, seed=3)
+    w1 = workload(np.ascontiguousarray(q2[:, :1]), [x[:-1] for x in logical], block_size=16, seed=3)
+    d2, d1 = upload(w2), upload(w1)
+    o2, l2 = md.mla_decode_dense(d2.q, d2.kv, d2.block_table, d2.seq_lens, scale=w2.scale, max_seq_len=2000)
+    o1, l1 = md.mla_decode_dense(d1.q, d1.kv, d1.block_table, d1.seq_lens, scale=w1.scale, max_seq_len=2000)
+    assert torch.equal(o2[:, 0], o1[:, 0]) and torch.equal(l2[:, 0], l1[:, 0])
+
+
+def test_repeated_runs_are_bitwise_identical():
+    w = W.make_workload("det", 4, 1, 128, [4096, 100, 2500, 3000], 64, seed=101, top_k=1024)
+    d = upload(w)
+    first = run(d)
+    for _ in range(5):
+        again = run(d)
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+
+
+def test_sparse_over_all_positions_matches_dense():
+    w = W.make_workload("all", 2, 1, 128, [1000, 640], 16, seed=111)
+    d = upload(w)
+    dense = run(d, out_dtype=torch.float32)
+    idx = np.full((2, 1000), -1, dtype=np.int32)
+    for b, S in enumerate([1000, 640]):
+        idx[b, :S] = np.random.default_rng(b).permutation(S)
+    sp = md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, torch.from_numpy(idx).cuda(),
+                              scale=w.scale, max_seq_len=w.max_seq_len, out_dtype=torch.float32)
+    ro, rl = oracle.dense(w)
+    for o, l in (dense, sp):
+        assert_o_close(o, ro, "all positions")
+        assert_lse_close(l, rl, "all positions")
+    # same attended set, different order and tiling: equal up to bf16 weight rounding
+    assert torch.allclose(dense[0], sp[0], atol=1e-2) and torch.allclose(dense[1], sp[1], atol=1e-4)
+
+
+def test_large_score_jump_takes_the_restart_path():
+    # Within the first 64-token tile, sub-block 0 (tokens 0..31) peaks at a score
+    # of 8 nats and token 40 (sub-block 1) scores 64 nats: 80 base-2 units more,
+    # beyond the in-loop headroom, so the work-group must recompute its unit.
+    rng = np.random.default_rng(121)
+    S = 3000
+    rows = random_rows(rng, S, std=0.05)
+    q = np.zeros((1, 1, 32, W.D_QK), dtype=np.uint16)
+    q[0, 0, :, 512] = bf16(64.0)
+    rows[:, 512] = bf16(0.0)
+    rows[10, 512] = bf16(1.0)             # score 64 * 1 * 0.125 = 8 nats
+    rows[40, 512] = bf16(8.0)             # score 64 nats
+    rows[2900, 512] = bf16(7.5)
+    w = workload(q, [rows], block_size=64, scale=0.125, seed=5)
+    out, lse = run(upload(w), out_dtype=torch.float32)
+    ro, rl = oracle.dense(w)
+    assert_o_close(out, ro, "restart")
+    assert_lse_close(lse, rl, "restart")
+
+
+def test_empty_sequences_and_fully_masked_rows():
+    w = W.make_workload("empty", 2, 1, 128, [64, 500], 64, seed=131, top_k=64)
+    w.indices = w.indices.copy()
+    w.indices[:64] = -1                     # sequence 0 attends nothing
+    out, lse = run(upload(w), out_dtype=torch.float32)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    ro, rl = oracle.sparse(w)
+    assert_o_close(out, ro)
+    assert_lse_close(lse, rl)
+
+
+# ---------------------------------------------------------------- full-size configs (sampled rows)
+
+def sampled_rows(w, n, seed):
+    g = np.random.default_rng(seed)
+    rows = set(g.choice(w.rows, size=min(n, w.rows), replace=False).tolist())
+    rows |= {0, w.rows - 1}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg,out_dtype", [(2, torch.bfloat16), (3, torch.bfloat16), (5, torch.bfloat16),
+                                           (5, torch.float32), (6, torch.bfloat16)])
+def test_full_size_config_sampled(cfg, out_dtype):
+    w = W.CONFIGS[cfg]()
+    d = upload(w)
+    out, lse = run(d, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w, 48, cfg)
+    ro, rl = oracle_of(w, rows=rows)
+    og = out.reshape(-1, 512)[torch.from_numpy(rows).cuda()]
+    lg = lse.reshape(-1)[torch.from_numpy(rows).cuda()]
+    assert_o_close(og, ro, w.name)
+    assert_lse_close(lg, rl, w.name)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_full_size_split_kv_config_sampled():
+    w = W.config_split_kv()
+    d = upload(w)
+    parts, lses = run(d)
+    merged, mlse = md.mla_merge_lse(parts, lses, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w, 24, 4)
+    idx = torch.from_numpy(rows).cuda()
+    for r in (0, 5):
+        ro, rl = oracle.dense(w, rows=rows, num_shards=8, interleave=64, shard_id=r)
+        assert_o_close(parts[r].reshape(-1, 512)[idx], ro, f"shard {r}")
+        assert_lse_close(lses[r].reshape(-1)[idx], rl, f"shard {r}")
+    ro, rl = oracle.dense(w, rows=rows)
+    assert_o_close(merged.reshape(-1, 512)[idx], ro, "merged")
+    assert_lse_close(mlse.reshape(-1)[idx], rl, "merged")
