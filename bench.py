@@ -1,0 +1,312 @@
+"""Benchmark: MLA decode throughput on one MI355X, in KV-token·heads/s.
+
+One step = one pass of the whole decode hot path (plan, attended-set and paged
+gather, QK^T, mask, online softmax, PV, finalize, split-KV merge) over one
+batch of synthetic, seeded inputs that are already resident in HBM.  The
+default workload is the DSA/SFA sparse decode: B=32, Q=1, h_q=128, S=32768,
+top_k=2048 (3 sequences keep 1500 entries), paged block_size 64, bf16.
+
+Cache effects: each timed step reads a different one of `--rotate` index sets
+(or cache copies for dense workloads), so the rows a step touches are not left
+in the 256 MiB Infinity Cache by the previous step.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, TFLOP/s
+METRIC = "sparse/dense MLA decode KV-token·heads/s at 1 GPU; % of HBM/MFMA roofline"
+KERNEL_SOURCES = [os.path.join(ROOT, "latent_decode_attention_amd", "csrc", f)
+                  for f in ("mla_kernels.hip", "mla_api.cpp", "mla_internal.h")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(w, indices_list=None):
+    """Bytes and flops the method must move/compute for one step.
+
+    bytes = latent rows attended (each once per sequence) x 1152 + q + O + lse
+            + index lists + block-table entries of the blocks touched
+            (+ the fp32 shard partials written and read, for sharded dense).
+    flops = sum_{b,q} |A(b,q)| * h_q * 2 * (576 + 512).
+    """
+    B, Q, H = w.B, w.Q, w.h_q
+    rows_bytes = 0
+    bt_bytes = 0
+    kv_heads = 0
+    for b in range(B):
+        S = int(w.seq_lens[b])
+        if w.indices is None:
+            need = set(range(S))                                  # every position, causal union
+            per_q = [max(0, S - Q + qi + 1) for qi in range(Q)]
+        else:
+            lst = indices_list[b] if indices_list is not None else w.indices.reshape(-1)[
+                b * w.index_stride_b: b * w.index_stride_b + w.top_k]
+            lst = np.asarray(lst)
+            need = set(int(i) for i in lst if 0 <= i <= S - 1)
+            per_q = [int(np.count_nonzero((lst >= 0) & (lst <= S - Q + qi))) for qi in range(Q)]
+        rows_bytes += len(need) * 1152
+        bt_bytes += len({p // w.block_size for p in need}) * 4
+        kv_heads += sum(per_q) * H
+    q_bytes = B * Q * H * 576 * 2
+    o_bytes = B * Q * H * 512 * 2
+    lse_bytes = B * Q * H * 4
+    idx_bytes = 0 if w.indices is None else B * (1 if w.index_stride_q == 0 else Q) * w.top_k * 4
+    extra = 0
+    if w.num_shards > 1:  # the formulation emits fp32 shard partials, written then read by the merge
+        o_bytes = B * Q * H * 512 * 2
+        extra = 2 * w.num_shards * B * Q * H * (512 + 1) * 4
+    total = rows_bytes + q_bytes + o_bytes + lse_bytes + idx_bytes + bt_bytes + extra
+    flops = kv_heads * 2 * (576 + 512)
+    return dict(bytes=total, flops=flops, kv_token_heads=kv_heads, rows_bytes=rows_bytes)
+
+
+def stored_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
+    kernel sources have not changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload_name)
+    if not ent or ent.get("kernel_hash") != kernel_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float, seed: int = 0):
+    """Time the fp64 oracle on a bounded sample of output rows of the same workload."""
+    import oracle
+    g = np.random.default_rng(seed)
+    rows_all = g.permutation(w.rows)
+    n = 16
+    spent = 0.0
+    done_rows = 0
+    done_work = 0
+    while spent < target_s and done_rows < w.rows:
+        sel = rows_all[done_rows:done_rows + n]
+        t0 = time.perf_counter()
+        if w.indices is not None:
+            oracle.sparse(w, rows=sel)
+        else:
+            oracle.dense(w, rows=sel)
+        spent += time.perf_counter() - t0
+        for r in sel:
+            b = int(r) // (w.Q * w.h_q)
+            qi = (int(r) // w.h_q) % w.Q
+            S = int(w.seq_lens[b])
+            if w.indices is None:
+                done_work += max(0, S - w.Q + qi + 1)
+            else:
+                lst = w.indices.reshape(-1)[b * w.index_stride_b + qi * w.index_stride_q:][:w.top_k]
+                done_work += int(np.count_nonzero((lst >= 0) & (lst <= S - w.Q + qi)))
+        done_rows += len(sel)
+        n = min(n * 2, 4096)
+    return dict(value=done_work / spent, unit="KV-token·heads/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"{done_rows} of {w.rows} output rows (b,q,head) of {w.name}, fp64, {spent:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload preset (1..6); 3 = sparse S=32k")
+    ap.add_argument("--rotate", type=int, default=8, help="distinct input sets cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the split-KV path runs "
+              "its shards on one device and no multi-GPU run is part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from latent_decode_attention_amd import mla_decode as md
+    from latent_decode_attention_amd import workloads as W
+    from latent_decode_attention_amd.device import bf16_tensor, upload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = W.CONFIGS[args.config]()
+    d = upload(w, dev)
+    print(f"[bench] workload {w.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    stream = torch.cuda.current_stream()
+
+    # Rotating inputs so consecutive steps touch different rows.
+    if w.indices is not None:
+        idx_host = [w.indices] + [W.rotate_indices(w, 1000 + r) for r in range(args.rotate - 1)]
+        idx_dev = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev) for x in idx_host]
+        kv_dev = [d.kv]
+    else:
+        idx_host, idx_dev = None, None
+        copies = max(1, min(args.rotate, int((2 << 30) // max(1, d.kv.numel() * 2))))
+        kv_dev = [d.kv] + [d.kv.clone() for _ in range(copies - 1)]
+
+    p0 = md.make_problem(d.q, d.kv, d.block_table, d.seq_lens, w.scale, w.max_seq_len)
+    plan = md.mla_plan_query(p0, num_shards=w.num_shards, interleave=w.interleave,
+                             top_k=w.top_k, index_stride_q=w.index_stride_q,
+                             num_cus=torch.cuda.get_device_properties(dev).multi_processor_count)
+    ws_bytes = md.mla_workspace_size(p0, w.num_shards, -1, w.top_k)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    sharded = w.num_shards > 1
+    if sharded:
+        out = torch.empty((w.num_shards, w.B, w.Q, w.h_q, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.num_shards, w.B, w.Q, w.h_q), dtype=torch.float32, device=dev)
+        merged = torch.empty((w.B, w.Q, w.h_q, 512), dtype=out_dtype, device=dev)
+        mlse = torch.empty((w.B, w.Q, w.h_q), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((w.B, w.Q, w.h_q, 512), dtype=out_dtype, device=dev)
+        lse = torch.empty((w.B, w.Q, w.h_q), dtype=torch.float32, device=dev)
+
+    def step(i):
+        r = i % len(kv_dev if idx_dev is None else idx_dev)
+        if idx_dev is not None:
+            md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, idx_dev[r], scale=w.scale,
+                                 max_seq_len=w.max_seq_len, top_k=w.top_k, index_stride_b=w.index_stride_b,
+                                 index_stride_q=w.index_stride_q, out=out, lse=lse,
+                                 workspace=workspace, stream=stream)
+        else:
+            md.mla_decode_dense(d.q, kv_dev[r], d.block_table, d.seq_lens, scale=w.scale,
+                                max_seq_len=w.max_seq_len, num_shards=w.num_shards, interleave=w.interleave,
+                                shard_id=-1, out=out, lse=lse, workspace=workspace, stream=stream)
+            if sharded:
+                md.mla_merge_lse(out, lse, out=merged, lse_out=mlse, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # The library's internal merge (split-KV partitions) is the only other kernel
+    # of a step: time it alone on the same partials and take it out to get the
+    # decode kernel's own duration.
+    merge_ms = 0.0
+    splits = plan["splits"]
+    groups_of_partials = plan["units"] // max(1, w.B * (w.Q // plan["q_per_group"])) if sharded else 1
+    # (With several shards the library merges all of them in one launch, which the
+    # public merge call cannot replay; decode_ms then conservatively keeps it.)
+    if splits > 1 and groups_of_partials == 1:
+        rows = w.B * w.Q * w.h_q
+        groups = 1
+        n_o = groups * splits * rows * 512
+        po = workspace[: n_o * 4].view(torch.float32).view(groups * splits, rows, 512)
+        pl_off = ((n_o * 4 + 255) // 256) * 256
+        pls = workspace[pl_off: pl_off + groups * splits * rows * 4].view(torch.float32).view(groups * splits, rows)
+        mo = torch.empty((rows, 512), dtype=torch.float32 if sharded else out_dtype, device=dev)
+        ml = torch.empty((rows,), dtype=torch.float32, device=dev)
+        po_g = po.view(groups, splits, rows, 512)
+        pl_g = pls.view(groups, splits, rows)
+        for _ in range(3):
+            for g in range(groups):
+                md.mla_merge_lse(po_g[g], pl_g[g], out=mo, lse_out=ml, stream=stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            for g in range(groups):
+                md.mla_merge_lse(po_g[g], pl_g[g], out=mo, lse_out=ml, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        merge_ms = ev0.elapsed_time(ev1) / args.steps
+    shard_merge_ms = 0.0
+    if sharded:
+        ev0.record(stream)
+        for _ in range(args.steps):
+            md.mla_merge_lse(out, lse, out=merged, lse_out=mlse, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        shard_merge_ms = ev0.elapsed_time(ev1) / args.steps
+    decode_ms = max(ms_per_step - merge_ms - shard_merge_ms, 1e-6)
+
+    # Work per step (averaged over the rotating index sets).
+    if idx_host is not None:
+        works = []
+        for x in idx_host:
+            lists = np.asarray(x).reshape(w.B, -1)[:, :w.top_k]
+            works.append(algorithmic_work(w, lists))
+        work = {k: float(np.mean([x[k] for x in works])) for k in works[0]}
+    else:
+        work = algorithmic_work(w)
+    value = work["kv_token_heads"] / (ms_per_step * 1e-3)
+    t_roof_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_roof_mfma = work["flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+    bound = "hbm" if t_roof_hbm >= t_roof_mfma else "mfma"
+    achieved_gbs = work["bytes"] / (decode_ms * 1e-3) / 1e9
+    traffic = stored_traffic(w.name)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV-token·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Q": w.Q, "h_q": w.h_q,
+                   "seq_len": int(w.max_seq_len), "top_k": w.top_k or None,
+                   "num_shards": w.num_shards, "block_size": w.block_size,
+                   "out_dtype": args.out_dtype, "rotating_input_sets": len(idx_dev or kv_dev),
+                   "split_kv_partitions": splits, "grid": plan["grid"]},
+        "roofline": {"bound": bound, "achieved": achieved_gbs if bound == "hbm" else work["flops"] / (decode_ms * 1e-3) / 1e12,
+                     "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_BF16_PEAK_TFS,
+                     "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                     "frac": (achieved_gbs / HBM_PEAK_GBS) if bound == "hbm" else
+                             (work["flops"] / (decode_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS),
+                     "traffic": traffic,
+                     "kernel": "decode_kernel", "kernel_ms": decode_ms,
+                     "mfma_tflops": work["flops"] / (decode_ms * 1e-3) / 1e12,
+                     "mfma_frac": work["flops"] / (decode_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                     "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
+                     "step_frac_of_roofline": max(t_roof_hbm, t_roof_mfma) / (ms_per_step * 1e-3),
+                     "merge_ms": merge_ms + shard_merge_ms},
+    }
+    print(f"[bench] {ms_per_step * 1e3:.1f} us/step, decode kernel {decode_ms * 1e3:.1f} us, "
+          f"merge {1e3 * (merge_ms + shard_merge_ms):.1f} us, {achieved_gbs:.0f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
