@@ -67,7 +67,7 @@ typedef struct {
   int32_t h_q;                /* query heads, 1..128 */
   int32_t d_qk;               /* latent row width; must be 576 */
   int32_t d_v;                /* value width (leading columns of the row); must be 512 */
-  float scale;                /* softmax scale applied to <q, k>, finite */
+  float scale;                /* softmax scale applied to <q, k>: finite and > 0 */
   const void *q;              /* device, bf16 [B, Q, h_q, d_qk] (query already absorbed
                                  into the latent space; RoPE part last) */
   const void *kv;             /* device, bf16 [num_blocks, block_size, d_qk] */

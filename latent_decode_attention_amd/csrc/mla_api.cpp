@@ -55,7 +55,7 @@ mla_status_t check_problem(const mla_problem_t *p) {
   if ((int64_t)p->num_blocks * p->block_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)p->max_seq_len > (int64_t)p->max_blocks * p->block_size) return MLA_ERR_BAD_SHAPE;
   if (p->max_seq_len < p->Q) return MLA_ERR_BAD_SHAPE;
-  if (!std::isfinite(p->scale)) return MLA_ERR_BAD_SHAPE;
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return MLA_ERR_BAD_SHAPE;
   if ((reinterpret_cast<uintptr_t>(p->q) | reinterpret_cast<uintptr_t>(p->kv)) & 15)
     return MLA_ERR_BAD_SHAPE;  // rows are moved in 16-byte pieces
   return MLA_OK;

@@ -1,25 +1,27 @@
 // MLA decode attention kernels for gfx950 (MI355X).
 //
 // One work-group (4 waves x 64 lanes) owns one (sequence, query-token group,
-// shard, KV partition) unit and streams that unit's latent rows through LDS in
-// 64-token tiles.  Every query head of the group dots the same latent row
-// (h_kv = 1 for MLA: "RFC: MsModeling 支持 Decode Context Parallel 仿真",
-// §2.1.4 symbol table), so per tile the work is two dense contractions that
-// run on the bf16 matrix cores:
-//   S^T[token, head] = K_tile[64 x 576] . Q^T[576 x 32]        (per wave)
-//   O^T[col, head]  += V_tile^T[512 x 64] . P^T[64 x 32]        (per wave)
-// with V_tile = the first 512 columns of the same LDS rows.  The softmax is
-// the online (running max / running sum) form; the KV partitions of one unit
-// and the DCP shards are combined by the same log-sum-exp merge the DCP page
-// describes (§1.1, §2.1.4.3).
+// shard, KV partition) unit of up to 128 query rows (query token x head) and
+// streams that unit's latent rows through LDS in 64-token tiles.  Every query
+// head dots the same latent row (h_kv = 1 for MLA: "RFC: MsModeling 支持
+// Decode Context Parallel 仿真", §2.1.4 symbol table), so per tile the work is
+// two dense contractions on the bf16 matrix cores:
+//   scores  S^T[token, row] = K_tile[64 x 576] . Q^T[576 x 32]    wave w: rows 32w..32w+31
+//   output  O^T[col, row]  += V_tile^T[128 x 64] . P^T[64 x 128]  wave w: cols 128w..128w+127
+// with V_tile = the first 512 columns of the same LDS rows.  Each wave turns
+// its scores into softmax weights P and publishes them in LDS; every wave then
+// multiplies all 128 rows' weights against its own quarter of the value
+// columns, so each transposed V operand read from LDS feeds four MFMAs.  The KV
+// partitions of a unit and the DCP shards are combined by the log-sum-exp merge
+// the DCP page describes (§1.1, §2.1.4.3).
 //
 // Data movement:
-//  * the block-table lookup (§2.1.4.1, table A) of tile t+2 and the sparse
-//    index load of tile t+3 are issued while tile t is being computed;
-//  * tile t+1 is copied HBM -> LDS with direct-to-LDS 16-byte loads
-//    (global_load_lds_dwordx4) while tile t is being computed; positions that
-//    are padding, out of range or beyond the causal limit are zero-filled in
-//    LDS and never read from memory;
+//  * every wave derives the positions, block-table rows (§2.1.4.1, table A) and
+//    attended masks of each tile itself: block ids two tiles ahead, positions
+//    three tiles ahead, so those loads complete under the math;
+//  * tile t+1 is copied HBM -> LDS with direct-to-LDS 16-byte loads spread over
+//    tile t's score loops; positions that are padding, out of range or beyond
+//    the causal limit are zero-filled in LDS and never read from memory;
 //  * an LDS tile holds 64 rows as 9 column groups of 128 bytes (8 chunks of
 //    16 bytes): group g of row r lives at g * 8192 + r * 128.  Within a group
 //    the chunks of row r are XOR-swizzled by a key of r mod 8 so that the K
@@ -36,7 +38,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -47,13 +48,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRowBytes = kDqk * 2;                           // 1152
-constexpr int kChunks = kRowBytes / 16;                       // 72
-constexpr int kTileBytes = kTile * kRowBytes;                 // 73728
-constexpr int kQkSteps = kDqk / 16;                           // 36 k-steps of the 32x32x16 MFMA
-constexpr int kGroups = kChunks / 8;                          // 9 column groups of 128 bytes
-constexpr int kGroupBytes = kTile * 128;                      // 8192
-constexpr int kColTiles = kDv / 32;                           // 16 output column tiles
+constexpr int kRowBytes = kDqk * 2;            // 1152
+constexpr int kChunks = kRowBytes / 16;        // 72
+constexpr int kTileBytes = kTile * kRowBytes;  // 73728
+constexpr int kQkSteps = kDqk / 16;            // 36 k-steps of the 32x32x16 MFMA
+constexpr int kGroups = kChunks / 8;           // 9 column groups of 128 bytes
+constexpr int kGroupBytes = kTile * 128;       // 8192
+constexpr int kCopySteps = 2 * kGroups;        // direct-load instructions per wave per tile
+constexpr int kAccTiles = 16;                  // 4 row tiles x 4 column tiles of 32 x 32
 // How far (base 2) a score may exceed its row's reference maximum before the
 // unit is recomputed with a higher reference: p <= 2^60 keeps sum(p) * |v| far
 // inside the fp32 range for any realistic row.
@@ -61,20 +63,26 @@ constexpr float kHeadroomLog2 = 60.0f;
 constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unconstrained
 
 static_assert(kTile == 16 * kWaves, "each wave copies 16 rows of a tile");
+static_assert(kMaxRowsPerGroup == 32 * kWaves, "each wave owns 32 query rows");
+static_assert(kQkSteps * 2 == 4 * kCopySteps, "one copy step every fourth score step");
+constexpr int kKAhead = 3;  // K operand reads in flight ahead of the MFMA that uses them
+
+// Source of the bytes copied for tokens that no query row attends, so that a
+// tile never holds stale or poisoned rows and the copies need no per-lane branch.
+__device__ __attribute__((aligned(256))) const unsigned kZeroRow[kRowBytes / 4] = {};
 
 struct __attribute__((aligned(16))) Smem {
-  char tile[2][kTileBytes];                   // double-buffered latent rows
-  int32_t row[2][kTile];                      // physical row per tile token, -1 = not loaded
-  unsigned long long mask[3][kMaxQPerGroup];  // attended-token bitmask per query token
-  int32_t restarts;                           // bumped when a row needs a higher reference
+  char tile[2][kTileBytes];  // double-buffered latent rows
+  // Softmax weights as MFMA B operands: [sub-block][owner wave][k-block][lane].
+  bf16x8 p[2][kWaves][2][64];
 };
-
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one work-group");
 
 // ---- Matrix-core helpers.  The 256 output accumulators of a lane fill the
 // whole AGPR file, so the MFMAs are written as inline asm with register-class
 // constraints (scores in VGPRs, outputs in AGPRs) to keep the allocator from
 // shuffling them.  Hazards the compiler cannot see through the asm are covered
-// by the fences below (s_nop counts exceed the 8-pass 32x32x16 MFMA's needs).
+// by the fences below (their s_nop counts exceed what the 32x32x16 MFMA needs).
 __device__ __forceinline__ void mfma_vgpr_first(f32x16 &d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
@@ -93,23 +101,16 @@ __device__ __forceinline__ void mfma_result_fence(f32x16 &d) {
   asm volatile("s_nop 15\n\ts_nop 3" : "+v"(d));
 }
 // VALU-written VGPRs -> MFMA operand reads.
-__device__ __forceinline__ void valu_result_fence(bf16x8 &a, bf16x8 &b) {
-  asm volatile("s_nop 3" : "+v"(a), "+v"(b));
-}
+__device__ __forceinline__ void operand_fence(bf16x8 &a) { asm volatile("s_nop 3" : "+v"(a)); }
 __device__ __forceinline__ void acc_result_fence(f32x16 *acc) {
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) asm volatile("" : "+a"(acc[ct]));
+  for (int i = 0; i < kAccTiles; ++i) asm volatile("" : "+a"(acc[i]));
 }
 
 __device__ __forceinline__ int chunk_key(int row) {
   const int x = row & 7;
   return ((x & 3) << 1) | (x >> 2);
-}
-
-// Byte offset in a tile of logical 16-byte chunk `lc` of tile row `r`.
-__device__ __forceinline__ int chunk_off(int r, int lc) {
-  return (lc >> 3) * kGroupBytes + r * 128 + (((lc ^ chunk_key(r)) & 7) << 4);
 }
 
 __device__ __forceinline__ int shard_len(int S, int N, int I, int r) {
@@ -127,7 +128,19 @@ struct Unit {
   int b, q0, shard, split;
   int S, i0, i1;
   int64_t idx_base;
+  const int32_t *bt;  // this sequence's block-table row
 };
+
+// Values the compiler cannot prove wave-uniform (loads from memory the kernel
+// might also write, 64-bit products) are moved to scalar registers explicitly.
+// Pointers stay kernel-argument base + uniform offset, so the compiler still
+// knows they address global memory.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 template <int kMode>
 __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
@@ -145,7 +158,7 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
   u.b = (int)(id / a.shard_units);
   u.q0 = qg * a.q_per_group;
   u.shard = a.shard_base + su;
-  u.S = a.seq_lens[u.b];
+  u.S = uniform(a.seq_lens[u.b]);
   int L;
   if constexpr (kMode == kSparseStream)
     L = a.top_k;
@@ -153,111 +166,103 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
     L = shard_len(u.S, a.num_shards, a.interleave, u.shard);
   else
     L = u.S > 0 ? u.S : 0;
-  u.i0 = u.split * a.chunk;
-  u.i1 = min(L, u.i0 + a.chunk);
-  u.idx_base = kMode == kSparseStream ? (int64_t)u.b * a.idx_stride_b + (int64_t)u.q0 * a.idx_stride_q : 0;
+  u.i0 = uniform(u.split * a.chunk);
+  u.i1 = uniform(min(L, u.i0 + a.chunk));
+  u.idx_base = kMode == kSparseStream ? uniform((int64_t)u.b * a.idx_stride_b + (int64_t)u.q0 * a.idx_stride_q) : 0;
+  u.bt = a.block_table + uniform((int64_t)u.b * a.max_blocks);
   return u;
 }
 
-// Logical token position of stream index i (dense: the position itself or the
-// i-th position owned by the shard; sparse: the i-th list entry).  -1 past the end.
+// ---- Per-tile token metadata, one token per lane.  The raw loads use clamped
+// (always in-bounds) addresses and are examined only after the tile's math, so
+// no wait on them lands in front of the math (a wait there would also drain
+// the in-flight copy of the next tile, which shares the vector-memory counter).
+
+// Stream index i -> logical position (dense: the position itself or the i-th
+// position the shard owns; sparse: the raw list entry, validated later).
 template <int kMode>
-__device__ __forceinline__ int stream_position(const DecodeArgs &a, const Unit &u, int i) {
-  if (i >= u.i1) return -1;
-  if constexpr (kMode == kSparseStream) return a.indices[u.idx_base + i];
+__device__ __forceinline__ int raw_position(const DecodeArgs &a, const Unit &u, int i) {
+  if constexpr (kMode == kSparseStream) return a.indices[u.idx_base + min(i, u.i1 - 1)];
   if constexpr (kMode == kShardStream)
     return ((i / a.interleave) * a.num_shards + u.shard) * a.interleave + (i % a.interleave);
   return i;
 }
-
-// Block-table entry for position p, or -1 when p is never attended by this
-// group's query tokens or the entry is out of range.
-__device__ __forceinline__ int lookup_block(const DecodeArgs &a, const Unit &u, int p) {
-  const int last = u.S - a.Q + u.q0 + a.q_per_group - 1;
-  if (p < 0 || p > last) return -1;
-  const int slot = p >> a.bs_shift;
-  if (slot >= a.max_blocks) return -1;
-  const int blk = a.block_table[(int64_t)u.b * a.max_blocks + slot];
-  return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
-}
-
-// Prefetch variants used inside the tile loop: the loads are unconditional with
-// clamped (always in-bounds) addresses and their values are only examined after
-// the tile's math, so no wait on them lands in front of the math (a wait there
-// would also drain the in-flight copy of the next tile).
-__device__ __forceinline__ int raw_index(const DecodeArgs &a, const Unit &u, int i) {
-  return a.indices[u.idx_base + min(i, u.i1 - 1)];
-}
 __device__ __forceinline__ int raw_block(const DecodeArgs &a, const Unit &u, int p) {
   const int slot = min(max(p, 0) >> a.bs_shift, a.max_blocks - 1);
-  return a.block_table[(int64_t)u.b * a.max_blocks + slot];
+  return u.bt[slot];
 }
-__device__ __forceinline__ int checked_block(const DecodeArgs &a, const Unit &u, int p, int raw) {
+// Physical cache row of a token, or -1 when no query row of this group attends it.
+__device__ __forceinline__ int token_row(const DecodeArgs &a, const Unit &u, int i, int p, int blk) {
   const int last = u.S - a.Q + u.q0 + a.q_per_group - 1;
-  const bool ok = p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && raw >= 0 &&
-                  raw < a.num_blocks;
-  return ok ? raw : -1;
+  const bool ok = i < u.i1 && p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && blk >= 0 &&
+                  blk < a.num_blocks;
+  return ok ? blk * a.block_size + (p & (a.block_size - 1)) : -1;
 }
 
-// Wave 0 publishes the physical rows and attended masks of one tile.
-__device__ __forceinline__ void publish_tile(Smem &sm, const DecodeArgs &a, const Unit &u,
-                                             int lane, int p, int blk, int row_buf, int mask_buf) {
-  const bool ok = blk >= 0;
-  sm.row[row_buf][lane] = ok ? blk * a.block_size + (p & (a.block_size - 1)) : -1;
-  for (int qq = 0; qq < a.q_per_group; ++qq) {
-    const unsigned long long m = __ballot(ok && p <= u.S - a.Q + u.q0 + qq);
-    if (lane == 0) sm.mask[mask_buf][qq] = m;
+// Attended-token bitmask of one tile for each query token of the group.
+struct TileMask {
+  unsigned long long m[kMaxQPerGroup];
+  bool full;  // every token attended by every query token of the group
+};
+__device__ __forceinline__ TileMask tile_mask(const DecodeArgs &a, const Unit &u, int p, int row) {
+  TileMask t;
+  unsigned long long all = ~0ull;
+#pragma unroll
+  for (int qq = 0; qq < kMaxQPerGroup; ++qq) {
+    t.m[qq] = qq < a.q_per_group ? __ballot(row >= 0 && p <= u.S - a.Q + u.q0 + qq) : 0ull;
+    if (qq < a.q_per_group) all &= t.m[qq];
   }
+  t.full = all == ~0ull;
+  return t;
 }
 
-// One direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// LDS address lds_base + 16 l.  The instruction's immediate offset is added to
-// both the global and the LDS address, so M0 is pre-biased by it.  Issued as
-// inline asm so that the compiler's memory model does not order it against the
-// other tile buffer's LDS reads (it would otherwise drain vmcnt before every
-// LDS access); completion is awaited explicitly with s_waitcnt vmcnt(0) before
-// the barrier that publishes the tile.
-// m0 is reserved for the compiler, which uses it for nothing else in these
-// kernels; the clobber records that the copy rewrites it.
+// ---- Direct global -> LDS copies.  One instruction moves 16 bytes per lane:
+// lane l's bytes land at LDS address M0 + 16 l.  Issued as inline asm so that
+// the compiler's memory model does not order it against the other buffer's LDS
+// reads (it would otherwise drain vmcnt before every LDS access); completion is
+// awaited explicitly with s_waitcnt vmcnt(0) before the barrier that publishes
+// the tile.  m0 is reserved for the compiler, which uses it for nothing else in
+// these kernels; the clobber records that the copy rewrites it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-template <int kOffset>
 __device__ __forceinline__ void dma16(const char *src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
-               :
-               : "s"(lds_base - kOffset), "v"(src), "i"(kOffset)
-               : "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_base), "v"(src) : "m0");
 }
 #pragma clang diagnostic pop
 
-template <int G>
-__device__ __forceinline__ void dma_row_groups(const char *src, unsigned lds_blk) {
-  dma16<G * 128>(src, lds_blk + G * kGroupBytes);
-  if constexpr (G + 1 < kGroups) dma_row_groups<G + 1>(src, lds_blk);
-}
+// Copy of one tile: wave w copies rows 16w..16w+15; step j moves 8 rows x 128
+// bytes of column group j % 9 of the 8-row block j / 9, lane l taking row
+// 16w + 8 (j / 9) + l / 8 and stored position l % 8 of it.  Rows nobody
+// attends (row index -1) are copied from the zero row.
+struct TileCopy {
+  const char *src[2];  // this lane's source bytes for the two 8-row blocks, group 0
+  unsigned lds[2];     // wave-uniform LDS address of each 8-row block, group 0
+};
 
-// All waves: copy one tile of latent rows into LDS buffer `buf`.  Wave w copies
-// rows 16w..16w+15; one instruction moves 8 rows x 128 bytes of one column
-// group, lane l taking row 16w + 8k + l/8 and stored position l%8 of it.
-__device__ __forceinline__ void issue_tile(Smem &sm, const DecodeArgs &a, int buf, int wave, int lane) {
+__device__ __forceinline__ TileCopy prepare_copy(Smem &sm, const DecodeArgs &a, int buf, int wave, int lane,
+                                                 int tile_row) {
+  TileCopy c;
   const char *kvb = reinterpret_cast<const char *>(a.kv);
-  const int sub = lane >> 3;                      // row within the 8-row block
-  const int lc_lo = (lane & 7) ^ chunk_key(sub);  // logical chunk (mod 8) at this slot
+  const int sub = lane >> 3;
+  const int lc = (lane & 7) ^ chunk_key(sub);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int r = 16 * wave + 8 * k + sub;
-    const int row = sm.row[buf][r];
-    const unsigned blk = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)(&sm.tile[buf][(16 * wave + 8 * k) * 128]));
-    if (row >= 0) {
-      dma_row_groups<0>(kvb + (int64_t)row * kRowBytes + lc_lo * 16, blk);
-    } else {
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g)
-        *reinterpret_cast<int4 *>(&sm.tile[buf][g * kGroupBytes + (16 * wave + 8 * k) * 128 + lane * 16]) =
-            make_int4(0, 0, 0, 0);
-    }
+    const int row = __shfl(tile_row, 16 * wave + 8 * k + sub);
+    c.src[k] = (row < 0 ? reinterpret_cast<const char *>(kZeroRow) : kvb + (int64_t)row * kRowBytes) + lc * 16;
+    const unsigned blk = (unsigned)(uintptr_t)(&sm.tile[buf][(16 * wave + 8 * k) * 128]);
+    c.lds[k] = __builtin_amdgcn_readfirstlane(blk);
   }
+  return c;
+}
+
+__device__ __forceinline__ void copy_step(const TileCopy &c, int j) {
+  const int k = j / kGroups, g = j % kGroups;
+  dma16(c.src[k] + g * 128, c.lds[k] + g * kGroupBytes);
+}
+
+__device__ __forceinline__ void copy_all(const TileCopy &c) {
+#pragma unroll
+  for (int j = 0; j < kCopySteps; ++j) copy_step(c, j);
 }
 
 // Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).  Vectors
@@ -286,45 +291,51 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const Unit u = decode_unit<kMode>(a);
   const int ntiles = u.i1 > u.i0 ? (u.i1 - u.i0 + kTile - 1) / kTile : 0;
 
-  // The wave's 32 query rows (q token, head); lane n and n+32 share a row.
-  const int row_local = wave * 32 + n;
-  const bool row_ok = row_local < a.rows_per_group;
-  const int q_local = row_ok ? row_local / a.h_q : 0;
-  const int head = row_ok ? row_local - q_local * a.h_q : 0;
-  const int64_t grow = ((int64_t)u.b * a.Q + u.q0 + q_local) * a.h_q + head;
-  const bool computes = wave * 32 < a.rows_per_group;
-
   // Output destination: final tensor or this partition's slot of the partials.
   const int64_t su = u.shard - a.shard_base;
   void *obase;
   float *lbase;
   int ofp32;
   if (a.splits > 1) {
-    const int64_t g = su * a.splits + u.split;
-    obase = a.part_o + g * a.rows_total * kDv;
-    lbase = a.part_lse + g * a.rows_total;
+    const int64_t g = uniform((su * a.splits + u.split) * a.rows_total);
+    obase = a.part_o + g * kDv;
+    lbase = a.part_lse + g;
     ofp32 = 1;
   } else {
+    const int64_t g = uniform(su * a.rows_total);
     ofp32 = a.out_fp32;
-    obase = ofp32 ? (void *)(reinterpret_cast<float *>(a.out) + su * a.rows_total * kDv)
-                  : (void *)(reinterpret_cast<__bf16 *>(a.out) + su * a.rows_total * kDv);
-    lbase = a.lse + su * a.rows_total;
+    obase = ofp32 ? (void *)(reinterpret_cast<float *>(a.out) + g * kDv)
+                  : (void *)(reinterpret_cast<__bf16 *>(a.out) + g * kDv);
+    lbase = a.lse + g;
   }
+  // Global output row of the group's query row r (query token r / h_q, head r % h_q).
+  auto out_row = [&](int r) -> int64_t {
+    const int ql = r / a.h_q;
+    return ((int64_t)u.b * a.Q + u.q0 + ql) * a.h_q + (r - ql * a.h_q);
+  };
+
+  // The wave's 32 query rows for the scores; lanes n and n + 32 share a row.
+  const int row_local = wave * 32 + n;
+  const bool row_ok = row_local < a.rows_per_group;
 
   if (ntiles == 0) {
+    // Nothing attended: O = 0, lse = -inf.
     if (row_ok) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      for (int c = half * 4; c < kDv; c += 8) store_out(obase, ofp32, grow * kDv + c, z);
-      if (half == 0) lbase[grow] = -INFINITY;
+      const int64_t gr = out_row(row_local);
+      for (int c = half * 4; c < kDv; c += 8) store_out(obase, ofp32, gr * kDv + c, z);
+      if (half == 0) lbase[gr] = -INFINITY;
     }
     return;
   }
+  const int q_local = row_ok ? row_local / a.h_q : 0;
 
   // Query rows in registers: lane (n, half) holds q[row][16 st + 8 half + 0..7], the
-  // B operand of the 32x32x16 MFMA for k-step st.
+  // B operand of the 32x32x16 MFMA for k-step st.  Rows past the group's end
+  // score 0 against everything; their outputs are never stored.
   bf16x8 qr[kQkSteps];
   if (row_ok) {
-    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + grow * kDqk);
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + out_row(row_local) * kDqk);
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
   } else {
@@ -333,237 +344,256 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   }
 
   // Per-lane LDS byte offsets within a tile.  K step st reads logical chunk
-  // 2 st + half of row n (+32 for the second sub-block): with the row's XOR key
-  // that is column group st / 4 (an immediate) plus one of four per-lane offsets.
-  // V step (kb, ct) reads column group ct / 2 (immediate) plus one of two.
-  const int key_k = chunk_key(n);
-  int k_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) k_off[j] = n * 128 + ((((2 * j + half) ^ key_k) & 7) << 4);
-  const int v_row = 4 * half + ((lane & 15) >> 2);    // row within a 16-token k-block
-  const int v_key = chunk_key(v_row);
-  const int v_lc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within a 64-byte span
-  int v_off[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) v_off[j] = v_row * 128 + ((((4 * j + v_lc) ^ v_key) & 7) << 4) + 8 * (lane & 1);
+  // 2 st + half of row n (+32 rows for the second sub-block): with the row's
+  // XOR key that is column group st / 4 (an immediate) plus the per-lane base
+  // with its chunk bits flipped by 2 (st % 4).  V reads of k-block kb and
+  // column tile ct: rows 16 kb + 4 half + (lane & 15) / 4 (+8), columns
+  // 128 wave + 32 ct + 16 ((lane >> 4) & 1) + 4 (lane & 3): column group
+  // 2 wave + ct / 2 plus the per-lane base with chunk bit 2 flipped for odd ct.
+  const int k_base = n * 128 + (((half ^ chunk_key(n)) & 7) << 4);
+  const int v_row = 4 * half + ((lane & 15) >> 2);
+  const int v_lc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int v_base = 2 * wave * kGroupBytes + v_row * 128 + (((v_lc ^ chunk_key(v_row)) & 7) << 4) + 8 * (lane & 1);
   const bf16x8 zero8 = {};
 
-  // Softmax bookkeeping, base-2 units.  m_ref is the row's reference maximum:
-  // set from the first sub-block in which the row attends anything, and only
-  // ever raised by a restart.  p = 2^(x - m_ref) may exceed 1 by up to
-  // 2^kHeadroom, which fp32 accumulators and bf16 operands carry without loss,
-  // so the accumulators are never rescaled inside the loop.
+  // Softmax bookkeeping for this wave's 32 rows, base-2 units.  m_ref is the
+  // row's reference maximum: set from the first sub-block in which the row
+  // attends anything, and only ever raised by a recompute pass.  p = 2^(x - m_ref)
+  // may exceed 1 by up to 2^kHeadroomLog2, which fp32 accumulators and bf16
+  // operands carry without loss, so the accumulators are never rescaled.
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;  // largest score seen so far
   float l_run = 0.f;         // this lane's share of sum(p), for lse
   float l_rnd = 0.f;         // the same sum over p as rounded to bf16, for O
-  f32x16 acc[kColTiles];
-  int restarts_seen = 0;
+  f32x16 acc[kAccTiles];     // acc[4 rt + ct]: rows 32 rt.., columns 128 wave + 32 ct..
 
-  if (tid == 0) sm.restarts = 0;
   for (;;) {
-    // Prologue of a pass: rows and masks of tiles 0 and 1; position of tile 2.
-    // (The opaque copy of the lane id keeps this per-pass work from being
-    // hoisted out of the restart loop and held in registers.)
-    int pf_pos = -1;
+    // ---- Prologue of a pass: rows and masks of tiles 0 and 1, positions of
+    // tile 2, copy of tile 0.  (The opaque lane copy keeps this per-pass work
+    // from being hoisted out of the pass loop and held in registers.)
     int plane = lane;
     asm volatile("" : "+v"(plane));
-    if (wave == 0) {
-      const int p0 = stream_position<kMode>(a, u, u.i0 + plane);
-      publish_tile(sm, a, u, plane, p0, lookup_block(a, u, p0), 0, 0);
-      if (ntiles > 1) {
-        const int p1 = stream_position<kMode>(a, u, u.i0 + kTile + plane);
-        publish_tile(sm, a, u, plane, p1, lookup_block(a, u, p1), 1, 1);
-      }
-      if (ntiles > 2) pf_pos = stream_position<kMode>(a, u, u.i0 + 2 * kTile + plane);
-    }
-    __syncthreads();
-    issue_tile(sm, a, 0, wave, lane);
+    const int p0 = raw_position<kMode>(a, u, u.i0 + plane);
+    const int row0 = token_row(a, u, u.i0 + plane, p0, raw_block(a, u, p0));
+    TileMask mask_cur = tile_mask(a, u, p0, row0);
+    const int p1 = raw_position<kMode>(a, u, u.i0 + kTile + plane);
+    int row_next = token_row(a, u, u.i0 + kTile + plane, p1, raw_block(a, u, p1));
+    TileMask mask_next = tile_mask(a, u, p1, row_next);
+    int p_2 = raw_position<kMode>(a, u, u.i0 + 2 * kTile + plane);
+    copy_all(prepare_copy(sm, a, 0, wave, lane, row0));
 
+    bf16x8 z = zero8;
+    operand_fence(z);  // the zero operand may have just been written by a VALU move
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) acc_zero(acc[ct], zero8);
+    for (int i = 0; i < kAccTiles; ++i) acc_zero(acc[i], z);
     l_run = 0.f;
     l_rnd = 0.f;
-    bool restart = false;
+    bool overflow = false;
 
     for (int t = 0; t < ntiles; ++t) {
       const int cur = t & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t have landed
-      __syncthreads();                       // ... and every other wave's
-      if (sm.restarts != restarts_seen) {    // uniform: read after the barrier
-        restart = true;
-        break;
-      }
-      if (t + 1 < ntiles) issue_tile(sm, a, cur ^ 1, wave, lane);
+      __syncthreads();                       // ... every wave's; tile t-1's P and V are consumed
+      // Lookups for later tiles, consumed after this tile's math.
+      const int i2 = u.i0 + (t + 2) * kTile + lane;
+      const int blk2_raw = raw_block(a, u, p_2);
+      const int p3_raw = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
+      // The copy of tile t+1 is spread over this tile's score loops, one
+      // instruction every fourth MFMA step, so it issues in the MFMAs' shadow.
+      const bool copy_next = t + 1 < ntiles;
+      const TileCopy next_copy = prepare_copy(sm, a, cur ^ 1, wave, lane, row_next);
 
-      // Start the lookups for later tiles so they complete under this tile's math
-      // (every wave issues them, only wave 0 uses them).
-      const bool pf2 = wave == 0 && t + 2 < ntiles;
-      const int i3 = u.i0 + (t + 3) * kTile + lane;
-      const int blk2_raw = raw_block(a, u, pf_pos);
-      int pos3_raw;
-      if constexpr (kMode == kSparseStream)
-        pos3_raw = raw_index(a, u, i3);
-      else
-        pos3_raw = stream_position<kMode>(a, u, i3);
-
-      if (computes) {
-        const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
-        // This lane's tokens are 4 half + {0..3} (+8 i, +32 sb): shift once so
-        // every bit test below uses a compile-time position.
-        const unsigned long long msk = sm.mask[t % 3][q_local] >> (4 * half);
-        bool overflow = false;
+      const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
+      // This lane's tokens are 4 half + {0..3} (+8 i, +32 sb): shift once so every
+      // bit test below uses a compile-time position.
+      unsigned long long msk = mask_cur.m[0];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          // ---- scores S^T = K . Q^T for the sub-block's 32 tokens.  Operands of
-          // step st+2 are read while step st multiplies (3-slot ring); the fences
-          // keep the compiler from hoisting every read.
-          f32x16 s;
-          bf16x8 kr[3];
-          auto k_read = [&](int st) {
-            return *(const bf16x8 LDS_AS *)(tb + k_off[st & 3] + (st >> 2) * kGroupBytes + sb * 32 * 128);
-          };
-          kr[0] = k_read(0);
-          kr[1] = k_read(1);
-#pragma unroll
-          for (int st = 0; st < kQkSteps; ++st) {
-            if (st + 2 < kQkSteps) kr[(st + 2) % 3] = k_read(st + 2);
-            if (st == 0)
-              mfma_vgpr_first(s, kr[0], qr[0]);
-            else
-              mfma_vgpr(s, kr[st % 3], qr[st]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          mfma_result_fence(s);
+      for (int qq = 1; qq < kMaxQPerGroup; ++qq)
+        if (q_local == qq) msk = mask_cur.m[qq];
+      msk = half ? msk >> 4 : msk;
+      asm volatile("" : "+v"(msk));  // select here, not inside the score loop
 
-          // ---- mask and scale.  Register r of lane (n, half) is token
-          // 8 (r / 4) + 4 half + r % 4 of the sub-block.
-          float x[16];
-          float smax = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        // ---- scores S^T = K . Q^T for the sub-block's 32 tokens.  The operand
+        // of step st + kKAhead is read while step st multiplies.
+        f32x16 s;
+        bf16x8 kr[kKAhead + 1];
+        auto k_read = [&](int st) {
+          return *(const bf16x8 LDS_AS *)(tb + (k_base ^ ((st & 3) << 5)) + (st >> 2) * kGroupBytes + sb * 32 * 128);
+        };
+#pragma unroll
+        for (int st = 0; st < kKAhead; ++st) kr[st] = k_read(st);
+#pragma unroll
+        for (int st = 0; st < kQkSteps; ++st) {
+          const int step = sb * kQkSteps + st;
+          if ((step & 3) == 0 && copy_next) copy_step(next_copy, step >> 2);
+          if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
+          if (st == 0)
+            mfma_vgpr_first(s, kr[0], qr[0]);
+          else
+            mfma_vgpr(s, kr[st % (kKAhead + 1)], qr[st]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_result_fence(s);
+
+        // ---- mask, weights.  Register r of lane (n, half) is token
+        // 8 (r / 4) + 4 half + r % 4 of the sub-block.  Scores stay unscaled
+        // until the exponent (the scale is positive, so the maximum commutes).
+        float x[16];
+        if (mask_cur.full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = s[r];
+        } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int bit = 32 * sb + 8 * (r >> 2) + (r & 3);
-            x[r] = ((msk >> bit) & 1ull) ? s[r] * a.scale_log2 : -INFINITY;
-            smax = fmaxf(smax, x[r]);
-          }
-          smax = fmaxf(smax, __shfl_xor(smax, 32));
-          m_seen = fmaxf(m_seen, smax);
-          if (m_ref == -INFINITY) m_ref = smax;  // first scores of this row: acc is still 0
-          overflow |= smax > m_ref + kHeadroomLog2;
-          const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-
-          bf16x8 pb[2];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              pv[e] = __builtin_amdgcn_exp2f(x[8 * k + e] - m_use);
-              l_run += pv[e];
-            }
-            const u32x4 w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
-                             pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
-            pb[k] = __builtin_bit_cast(bf16x8, w);
-            // O is normalised by the sum of the bf16 weights the MFMA actually
-            // used, so it stays an exact convex combination of the V rows.
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              l_rnd += __builtin_bit_cast(float, w[e] << 16) + __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
-          }
-          valu_result_fence(pb[0], pb[1]);
-
-          // ---- O^T += V^T . P^T, 16 tokens per MFMA.  The transposed LDS read
-          // gives lane (m, half) V[token(half, e)][32 ct + m] for e = 0..3 (rows
-          // +0..3) and e = 4..7 (rows +8..11): the k order of P^T above.
-          // Step i = 16 kb + ct; operands of step i+2 are read during step i.
-          i16x4 vr[3][2];
-          auto v_read = [&](int i, i16x4 *dst) {
-            const int kb = i >> 4, ct = i & 15;
-            const char LDS_AS *va0 = tb + v_off[ct & 1] + (ct >> 1) * kGroupBytes + (32 * sb + 16 * kb) * 128;
-            dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)va0);
-            dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(va0 + 8 * 128));
-          };
-          v_read(0, vr[0]);
-          v_read(1, vr[1]);
-#pragma unroll
-          for (int i = 0; i < 2 * kColTiles; ++i) {
-            if (i + 2 < 2 * kColTiles) v_read(i + 2, vr[(i + 2) % 3]);
-            const bf16x8 va = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(vr[i % 3][0], vr[i % 3][1], 0, 1, 2, 3, 4, 5, 6, 7));
-            mfma_agpr(acc[i & 15], va, pb[i >> 4]);
-            __builtin_amdgcn_sched_barrier(0);
+            x[r] = ((msk >> bit) & 1ull) ? s[r] : -INFINITY;
           }
         }
-        if (__any(overflow)) sm.restarts = restarts_seen + 1;
+        float smax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, x[r]);
+        smax = fmaxf(smax, __shfl_xor(smax, 32)) * a.scale_log2;
+        m_seen = fmaxf(m_seen, smax);
+        if (m_ref == -INFINITY) m_ref = smax;  // first scores of this row: acc is still 0
+        overflow |= smax > m_ref + kHeadroomLog2;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * k + e], a.scale_log2, -m_use));
+            l_run += pv[e];
+          }
+          const u32x4 w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
+                           pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
+          // O is normalised by the sum of the bf16 weights the MFMA actually
+          // used, so it stays an exact convex combination of the V rows.
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            l_rnd += __builtin_bit_cast(float, w[e] << 16) + __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+          // P^T operand of k-block 2 sb + k: lane (row n, half) holds tokens
+          // 16 k + 8 (e / 4) + 4 half + e % 4 of the sub-block.
+          sm.p[sb][wave][k][lane] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
+      __syncthreads();  // every wave's weights for this tile are in LDS
+
+      // ---- O^T += V^T . P^T for this wave's 128 columns and all 128 rows.
+      // The transposed LDS read gives lane (m, half) V[token(half, e)][col m]
+      // for e = 0..3 (rows +0..3) and e = 4..7 (rows +8..11): the k order of P^T.
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        bf16x8 pr[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) pr[rt] = sm.p[kb >> 1][rt][kb & 1][lane];
+        i16x4 vr[2][2];
+        auto v_read = [&](int ct, i16x4 *dst) {
+          const char LDS_AS *va0 = tb + (v_base ^ ((ct & 1) << 6)) + (ct >> 1) * kGroupBytes + 16 * kb * 128;
+          dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)va0);
+          dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(va0 + 8 * 128));
+        };
+        v_read(0, vr[0]);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          if (ct + 1 < 4) v_read(ct + 1, vr[(ct + 1) & 1]);
+          bf16x8 va = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(vr[ct & 1][0], vr[ct & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          operand_fence(va);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[rt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
-      if (pf2) publish_tile(sm, a, u, lane, pf_pos, checked_block(a, u, pf_pos, blk2_raw), cur, (t + 2) % 3);
-      pf_pos = i3 < u.i1 ? pos3_raw : -1;
+      // ---- metadata of tile t+2 (its lookups had the whole tile to land)
+      const int row2 = token_row(a, u, i2, p_2, blk2_raw);
+      mask_cur = mask_next;
+      mask_next = tile_mask(a, u, p_2, row2);
+      row_next = row2;
+      p_2 = p3_raw;
     }
-    if (!restart) {
-      __syncthreads();
-      restart = sm.restarts != restarts_seen;
-    }
-    if (!restart) break;
-    // Some row's scores outgrew its reference by more than the headroom: redo
-    // the unit with every reference raised to the largest score seen.
-    ++restarts_seen;
+
+    // ---- recompute vote: did any row outgrow its reference?  (The tile
+    // buffers are free once every wave is past the last tile.)
+    __syncthreads();
+    int *vote = reinterpret_cast<int *>(sm.tile[0]);
+    if (lane == 0) vote[wave] = __any(overflow) ? 1 : 0;
+    __syncthreads();
+    const bool redo = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+    __syncthreads();
+    if (!redo) break;
+    // Redo the unit with every reference raised to the largest score seen.
     m_ref = m_seen;
   }
 
-  if (!row_ok) return;
-  // The two lanes of a row saw disjoint halves of every tile.
+  // ---- finalize.  Each wave's outputs cover all rows, so the rounded row
+  // sums go through LDS (the tile buffers are free now).
+  float *l_sh = reinterpret_cast<float *>(sm.tile[0]);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float l_rnd_tot = l_rnd + __shfl_xor(l_rnd, 32);
-  const float inv = l_rnd_tot > 0.f ? 1.f / l_rnd_tot : 0.f;
-  if (half == 0)
-    lbase[grow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  if (half == 0) {
+    l_sh[row_local] = l_rnd_tot;
+    if (row_ok)
+      lbase[out_row(row_local)] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+  __syncthreads();
   acc_result_fence(acc);
-  // acc[ct] register 4i+j of lane (n, half) is column 32 ct + 8 i + 4 half + j.
+  // acc[4 rt + ct] register 4 i + j of lane (n, half) is row 32 rt + n, column
+  // 128 wave + 32 ct + 8 i + 4 half + j.
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) {
-    const f32x16 v = acc[ct];
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = 32 * rt + n;
+    const float l = l_sh[r];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const bool ok = r < a.rows_per_group;
+    const int64_t gr = ok ? out_row(r) : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 o = {v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv};
-      store_out(obase, ofp32, grow * kDv + 32 * ct + 8 * i + 4 * half, o);
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x16 v = acc[4 * rt + ct];
+      if (ok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 o = {v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv};
+          store_out(obase, ofp32, gr * kDv + 128 * wave + 32 * ct + 8 * i + 4 * half, o);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// (O, lse) merge: one work-group per (group, row); weights in LDS, fixed order.
-__global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
-  __shared__ float w[1024];
-  __shared__ float stats[2];
+// (O, lse) merge: one work-group per (group, row).  The n lse values go to LDS
+// in one cooperative load; every thread then derives the maximum and the
+// weight sum from LDS in the same fixed order and owns four consecutive columns.
+constexpr int kMergeThreads = 128;
+constexpr int kMaxMerge = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a) {
+  __shared__ float lse_sh[kMaxMerge];
   const int64_t r = blockIdx.x;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const float *lse = a.lse_parts + (int64_t)g * a.n * a.rows + r;
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int i = 0; i < a.n; ++i) M = fmaxf(M, lse[(int64_t)i * a.rows]);
-    float W = 0.f;
-    for (int i = 0; i < a.n; ++i) {
-      const float li = lse[(int64_t)i * a.rows];
-      const float wi = (M == -INFINITY || li == -INFINITY) ? 0.f : expf(li - M);
-      w[i] = wi;
-      W += wi;
-    }
-    stats[0] = M;
-    stats[1] = W;
-  }
+  for (int i = tid; i < a.n; i += kMergeThreads) lse_sh[i] = lse[(int64_t)i * a.rows];
   __syncthreads();
-  const float M = stats[0], W = stats[1];
+  float M = -INFINITY;
+  for (int i = 0; i < a.n; ++i) M = fmaxf(M, lse_sh[i]);
+  float W = 0.f;
+  if (M != -INFINITY)
+    for (int i = 0; i < a.n; ++i) W += lse_sh[i] == -INFINITY ? 0.f : expf(lse_sh[i] - M);
   const float inv = W > 0.f ? 1.f / W : 0.f;
   const int64_t out_row = (int64_t)g * a.rows + r;
-  for (int c = tid * 4; c < a.d_v; c += 128 * 4) {
+  for (int c = tid * 4; c < a.d_v; c += kMergeThreads * 4) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < a.n; ++i) {
-      if (w[i] == 0.f) continue;
+      const float li = lse_sh[i];
+      if (M == -INFINITY || li == -INFINITY) continue;
       const f32x4 o = *reinterpret_cast<const f32x4 *>(
           a.o_parts + (((int64_t)g * a.n + i) * a.rows + r) * a.d_v + c);
-      s += w[i] * o;
+      s += expf(li - M) * o;
     }
     store_out(a.out, a.out_fp32, out_row * a.d_v + c, s * inv);
   }
@@ -583,7 +613,8 @@ hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t strea
 }
 
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)args.rows, (unsigned)args.groups), dim3(128), 0,
+  if (args.n > kMaxMerge) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)args.rows, (unsigned)args.groups), dim3(kMergeThreads), 0,
                      stream, args);
   return hipGetLastError();
 }

@@ -59,6 +59,7 @@ def dense_status(p, num_shards=1, interleave=1, shard_id=-1, out=FAKE, dtype=0, 
     (dict(d_qk=512), 3), (dict(d_v=576), 3), (dict(h_q=129), 3), (dict(Q=17), 3),
     (dict(B=0), 2), (dict(h_q=0), 2), (dict(block_size=48), 2), (dict(block_size=0), 2),
     (dict(max_seq_len=2049 + 31 * 64), 2), (dict(max_seq_len=0), 2), (dict(scale=float("nan")), 2),
+    (dict(scale=0.0), 2), (dict(scale=-0.07), 2),
     (dict(q=FAKE + 8), 2),
 ])
 def test_dense_validation_statuses(kw, status):
