@@ -235,34 +235,44 @@ __device__ __forceinline__ void dma16(const char *src, unsigned lds_base) {
 // 16w + 8 (j / 9) + l / 8 and stored position l % 8 of it.  Rows nobody
 // attends (row index -1) are copied from the zero row.
 struct TileCopy {
-  const char *src[2];  // this lane's source bytes for the two 8-row blocks, group 0
-  unsigned lds[2];     // wave-uniform LDS address of each 8-row block, group 0
+  int row[2];       // this lane's cache row in each 8-row block (-1: the zero row)
+  int chunk;        // byte offset of this lane's 16-byte chunk within a column group
+  unsigned lds[2];  // wave-uniform LDS address of each 8-row block, group 0
 };
 
 __device__ __forceinline__ TileCopy prepare_copy(Smem &sm, const DecodeArgs &a, int buf, int wave, int lane,
                                                  int tile_row) {
   TileCopy c;
-  const char *kvb = reinterpret_cast<const char *>(a.kv);
   const int sub = lane >> 3;
-  const int lc = (lane & 7) ^ chunk_key(sub);
+  c.chunk = ((lane & 7) ^ chunk_key(sub)) * 16;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int row = __shfl(tile_row, 16 * wave + 8 * k + sub);
-    c.src[k] = (row < 0 ? reinterpret_cast<const char *>(kZeroRow) : kvb + (int64_t)row * kRowBytes) + lc * 16;
+    c.row[k] = __shfl(tile_row, 16 * wave + 8 * k + sub);
     const unsigned blk = (unsigned)(uintptr_t)(&sm.tile[buf][(16 * wave + 8 * k) * 128]);
     c.lds[k] = __builtin_amdgcn_readfirstlane(blk);
   }
   return c;
 }
 
-__device__ __forceinline__ void copy_step(const TileCopy &c, int j) {
+__device__ __forceinline__ void copy_step(const DecodeArgs &a, const TileCopy &c, int j) {
   const int k = j / kGroups, g = j % kGroups;
-  dma16(c.src[k] + g * 128, c.lds[k] + g * kGroupBytes);
+  const int row = c.row[k];
+  const char *base = row < 0 ? reinterpret_cast<const char *>(kZeroRow)
+                             : reinterpret_cast<const char *>(a.kv) + (int64_t)row * kRowBytes;
+  dma16(base + c.chunk + g * 128, c.lds[k] + g * kGroupBytes);
 }
 
-__device__ __forceinline__ void copy_all(const TileCopy &c) {
+__device__ __forceinline__ void copy_all(const DecodeArgs &a, const TileCopy &c) {
 #pragma unroll
-  for (int j = 0; j < kCopySteps; ++j) copy_step(c, j);
+  for (int j = 0; j < kCopySteps; ++j) copy_step(a, c, j);
+}
+
+// acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 with (1, 1)).
+// Written as asm: the compiler's own lowering of the dot2 builtin misplaced its
+// operands in this kernel.
+__device__ __forceinline__ float sum_bf16_pair(float acc, unsigned w, unsigned ones) {
+  asm("v_dot2c_f32_bf16 %0, %1, %2" : "+v"(acc) : "v"(w), "v"(ones));
+  return acc;
 }
 
 // Two floats to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).  Vectors
@@ -330,17 +340,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   }
   const int q_local = row_ok ? row_local / a.h_q : 0;
 
+  // ---- Start of a pass: the memory chain positions -> block ids -> rows ->
+  // copy of tile 0, with the positions of tiles 0..2 and the block ids of
+  // tiles 0 and 1 each fetched in one round trip.  Leaves the masks of tile 0
+  // and the raw lookups of tiles 1 and 2 for the tile loop.  (The opaque lane
+  // copy keeps this per-pass work from being hoisted and held in registers.)
+  TileMask mask_cur;
+  int pn1, bn1, pn2;
+  auto start_pass = [&]() {
+    int plane = lane;
+    asm volatile("" : "+v"(plane));
+    const int p0 = raw_position<kMode>(a, u, u.i0 + plane);
+    pn1 = raw_position<kMode>(a, u, u.i0 + kTile + plane);
+    pn2 = raw_position<kMode>(a, u, u.i0 + 2 * kTile + plane);
+    const int b0 = raw_block(a, u, p0);
+    bn1 = raw_block(a, u, pn1);
+    const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
+    copy_all(a, prepare_copy(sm, a, 0, wave, lane, row0));
+    mask_cur = tile_mask(a, u, p0, row0);
+  };
+  start_pass();
+
   // Query rows in registers: lane (n, half) holds q[row][16 st + 8 half + 0..7], the
-  // B operand of the 32x32x16 MFMA for k-step st.  Rows past the group's end
-  // score 0 against everything; their outputs are never stored.
+  // B operand of the 32x32x16 MFMA for k-step st.  Loaded after the copy of
+  // tile 0 is under way, so the two share the memory pipeline; the first
+  // tile's wait covers both.  Rows past the group's end load the group's first
+  // row instead (no branch around the loads); their outputs are never stored.
   bf16x8 qr[kQkSteps];
-  if (row_ok) {
-    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + out_row(row_local) * kDqk);
+  {
+    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + out_row(row_ok ? row_local : 0) * kDqk);
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
-  } else {
-#pragma unroll
-    for (int st = 0; st < kQkSteps; ++st) qr[st] = bf16x8{};
   }
 
   // Per-lane LDS byte offsets within a tile.  K step st reads logical chunk
@@ -355,6 +385,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int v_lc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int v_base = 2 * wave * kGroupBytes + v_row * 128 + (((v_lc ^ chunk_key(v_row)) & 7) << 4) + 8 * (lane & 1);
   const bf16x8 zero8 = {};
+  unsigned ones2 = 0x3F803F80u;  // (1.0, 1.0) in bf16, kept in a register
+  asm volatile("" : "+v"(ones2));
 
   // Softmax bookkeeping for this wave's 32 rows, base-2 units.  m_ref is the
   // row's reference maximum: set from the first sub-block in which the row
@@ -368,20 +400,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   f32x16 acc[kAccTiles];     // acc[4 rt + ct]: rows 32 rt.., columns 128 wave + 32 ct..
 
   for (;;) {
-    // ---- Prologue of a pass: rows and masks of tiles 0 and 1, positions of
-    // tile 2, copy of tile 0.  (The opaque lane copy keeps this per-pass work
-    // from being hoisted out of the pass loop and held in registers.)
-    int plane = lane;
-    asm volatile("" : "+v"(plane));
-    const int p0 = raw_position<kMode>(a, u, u.i0 + plane);
-    const int row0 = token_row(a, u, u.i0 + plane, p0, raw_block(a, u, p0));
-    TileMask mask_cur = tile_mask(a, u, p0, row0);
-    const int p1 = raw_position<kMode>(a, u, u.i0 + kTile + plane);
-    int row_next = token_row(a, u, u.i0 + kTile + plane, p1, raw_block(a, u, p1));
-    TileMask mask_next = tile_mask(a, u, p1, row_next);
-    int p_2 = raw_position<kMode>(a, u, u.i0 + 2 * kTile + plane);
-    copy_all(prepare_copy(sm, a, 0, wave, lane, row0));
-
     bf16x8 z = zero8;
     operand_fence(z);  // the zero operand may have just been written by a VALU move
 #pragma unroll
@@ -394,24 +412,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const int cur = t & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t have landed
       __syncthreads();                       // ... every wave's; tile t-1's P and V are consumed
-      // Lookups for later tiles, consumed after this tile's math.
-      const int i2 = u.i0 + (t + 2) * kTile + lane;
-      const int blk2_raw = raw_block(a, u, p_2);
-      const int p3_raw = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
+      // Rows and masks of tile t+1 from lookups that landed with the wait above.
+      const int row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
+      const TileMask mask1 = tile_mask(a, u, pn1, row1);
+      // Raw lookups two and three tiles ahead, examined only at the next tile's
+      // top (after its wait), so no wait on them falls inside this tile.
+      const int bn2 = raw_block(a, u, pn2);
+      const int pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
       // The copy of tile t+1 is spread over this tile's score loops, one
       // instruction every fourth MFMA step, so it issues in the MFMAs' shadow.
       const bool copy_next = t + 1 < ntiles;
-      const TileCopy next_copy = prepare_copy(sm, a, cur ^ 1, wave, lane, row_next);
+      const TileCopy next_copy = prepare_copy(sm, a, cur ^ 1, wave, lane, row1);
 
       const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
-      // This lane's tokens are 4 half + {0..3} (+8 i, +32 sb): shift once so every
-      // bit test below uses a compile-time position.
-      unsigned long long msk = mask_cur.m[0];
-#pragma unroll
-      for (int qq = 1; qq < kMaxQPerGroup; ++qq)
-        if (q_local == qq) msk = mask_cur.m[qq];
-      msk = half ? msk >> 4 : msk;
-      asm volatile("" : "+v"(msk));  // select here, not inside the score loop
 
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
         for (int st = 0; st < kQkSteps; ++st) {
           const int step = sb * kQkSteps + st;
-          if ((step & 3) == 0 && copy_next) copy_step(next_copy, step >> 2);
+          if ((step & 3) == 0 && copy_next) copy_step(a, next_copy, step >> 2);
           if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
           if (st == 0)
             mfma_vgpr_first(s, kr[0], qr[0]);
@@ -445,6 +458,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] = s[r];
         } else {
+          // This lane's tokens are 4 half + {0..3} (+8 i, +32 sb): shift once so
+          // every bit test uses a compile-time position.
+          unsigned long long msk = mask_cur.m[0];
+#pragma unroll
+          for (int qq = 1; qq < kMaxQPerGroup; ++qq)
+            if (q_local == qq) msk = mask_cur.m[qq];
+          msk = half ? msk >> 4 : msk;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int bit = 32 * sb + 8 * (r >> 2) + (r & 3);
@@ -472,8 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           // O is normalised by the sum of the bf16 weights the MFMA actually
           // used, so it stays an exact convex combination of the V rows.
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            l_rnd += __builtin_bit_cast(float, w[e] << 16) + __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+          for (int e = 0; e < 4; ++e) l_rnd = sum_bf16_pair(l_rnd, w[e], ones2);
           // P^T operand of k-block 2 sb + k: lane (row n, half) holds tokens
           // 16 k + 8 (e / 4) + 4 half + e % 4 of the sub-block.
           sm.p[sb][wave][k][lane] = __builtin_bit_cast(bf16x8, w);
@@ -508,12 +527,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         }
       }
 
-      // ---- metadata of tile t+2 (its lookups had the whole tile to land)
-      const int row2 = token_row(a, u, i2, p_2, blk2_raw);
-      mask_cur = mask_next;
-      mask_next = tile_mask(a, u, p_2, row2);
-      row_next = row2;
-      p_2 = p3_raw;
+      mask_cur = mask1;
+      pn1 = pn2;
+      bn1 = bn2;
+      pn2 = pn3;
     }
 
     // ---- recompute vote: did any row outgrow its reference?  (The tile
@@ -527,6 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if (!redo) break;
     // Redo the unit with every reference raised to the largest score seen.
     m_ref = m_seen;
+    start_pass();
   }
 
   // ---- finalize.  Each wave's outputs cover all rows, so the rounded row
