@@ -30,7 +30,7 @@ struct Plan {
   int q_per_group, rows_per_group, q_groups, shard_units;
   int units, splits, chunk, stream_len;
   int64_t grid;
-  size_t ws_o, ws_lse, ws_total;
+  size_t ws_o, ws_lse, ws_scale, ws_total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -104,13 +104,16 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   if (pl->grid > INT32_MAX) return MLA_ERR_BAD_SHAPE;
   const int64_t rows_total = (int64_t)p->B * p->Q * p->h_q;
   if (splits > 1) {
+    // Sized for fp32 partials; bf16-output calls store fp16 partials in the
+    // same region plus one inverse scale per (row, 128-column quarter).
     const int64_t parts = (int64_t)pl->shard_units * splits;
     pl->ws_o = align256((size_t)(parts * rows_total * kDv) * sizeof(float));
     pl->ws_lse = align256((size_t)(parts * rows_total) * sizeof(float));
+    pl->ws_scale = align256((size_t)(parts * rows_total * (kDv / 128)) * sizeof(float));
   } else {
-    pl->ws_o = pl->ws_lse = 0;
+    pl->ws_o = pl->ws_lse = pl->ws_scale = 0;
   }
-  pl->ws_total = pl->ws_o + pl->ws_lse;
+  pl->ws_total = pl->ws_o + pl->ws_lse + pl->ws_scale;
   return MLA_OK;
 }
 
@@ -166,8 +169,12 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
   a.out_fp32 = out_fp32 ? 1 : 0;
   a.lse = lse;
   if (pl.splits > 1) {
-    a.part_o = static_cast<float *>(workspace);
+    a.part_o = workspace;
     a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_o);
+    a.part_scale = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_o + pl.ws_lse);
+    // bf16 results keep fp16 partials: 2^-11 relative error, a quarter of the
+    // final bf16 rounding step; fp32 results keep fp32 partials.
+    a.part_f16 = out_fp32 ? 0 : 1;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_decode(a, pl.grid, s) != hipSuccess) return MLA_ERR_LAUNCH;
@@ -175,6 +182,8 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
     MergeArgs m;
     m.o_parts = a.part_o;
     m.lse_parts = a.part_lse;
+    m.scale_parts = a.part_scale;
+    m.f16 = a.part_f16;
     m.n = pl.splits;
     m.rows = a.rows_total;
     m.d_v = kDv;
@@ -248,6 +257,8 @@ mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t
   MergeArgs m;
   m.o_parts = o_parts;
   m.lse_parts = lse_parts;
+  m.scale_parts = nullptr;
+  m.f16 = 0;
   m.n = n;
   m.rows = rows;
   m.d_v = d_v;

@@ -36,14 +36,20 @@ struct DecodeArgs {
   void *out;
   int32_t out_fp32;
   float *lse;
-  // split-KV partial results (splits > 1): [shard_units * splits, rows_total, 512] and lse
-  float *part_o;
+  // split-KV partial results (splits > 1): O [shard_units * splits, rows_total, 512] as fp32,
+  // or (part_f16) as fp16 scaled per (row, 128-column quarter) with the inverse scales in
+  // part_scale [shard_units * splits, rows_total, 4]; lse [shard_units * splits, rows_total]
+  void *part_o;
   float *part_lse;
+  float *part_scale;
+  int32_t part_f16;
 };
 
 struct MergeArgs {
-  const float *o_parts;   // [groups * n, rows, d_v]
+  const void *o_parts;    // [groups * n, rows, d_v], fp32, or fp16 when f16
   const float *lse_parts; // [groups * n, rows]
+  const float *scale_parts;  // f16 only: [groups * n, rows, d_v / 128] inverse scales
+  int32_t f16;
   int32_t n;
   int64_t rows;
   int32_t d_v;

@@ -39,6 +39,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -106,6 +107,15 @@ __device__ __forceinline__ void acc_result_fence(f32x16 *acc) {
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");
 #pragma unroll
   for (int i = 0; i < kAccTiles; ++i) asm volatile("" : "+a"(acc[i]));
+}
+
+// Work-group barrier that orders LDS accesses only.  __syncthreads() also
+// waits for this wave's outstanding global stores (a full memory round trip),
+// which the epilogue's LDS exchange does not need.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ int chunk_key(int row) {
@@ -282,13 +292,38 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-__device__ __forceinline__ void store_out(void *out, int fp32, int64_t elem, f32x4 v) {
-  if (fp32) {
+// Two floats to packed fp16 (round to nearest even).
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
+__device__ __forceinline__ float half_bits_to_float(unsigned bits) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
+}
+
+// Element types of an output or partial buffer.
+enum OutKind { kOutBf16 = 0, kOutFp32 = 1, kOutFp16 = 2 };
+
+__device__ __forceinline__ void store_out(void *out, int kind, int64_t elem, f32x4 v) {
+  if (kind == kOutFp32) {
     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + elem) = v;
-  } else {
+  } else if (kind == kOutBf16) {
     const u32x2 h = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     *reinterpret_cast<u32x2 *>(reinterpret_cast<__bf16 *>(out) + elem) = h;
+  } else {
+    const u32x2 h = {pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+    *reinterpret_cast<u32x2 *>(reinterpret_cast<_Float16 *>(out) + elem) = h;
   }
+}
+
+// Power-of-two scale for storing values of magnitude up to `vmax` as fp16: the
+// largest lands in [2^14, 2^15), so every value keeps fp16's 11-bit precision
+// down to 2^-28 of the maximum.  Returns the scale; *inv gets its exact inverse.
+__device__ __forceinline__ float fp16_scale(float vmax, float *inv) {
+  int e = (int)((__builtin_bit_cast(unsigned, vmax) >> 23) & 255u) - 127;
+  e = max(-110, min(e, 127));
+  *inv = __builtin_bit_cast(float, (unsigned)(e - 14 + 127) << 23);
+  return __builtin_bit_cast(float, (unsigned)(14 - e + 127) << 23);
 }
 
 template <int kMode>
@@ -305,17 +340,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int64_t su = u.shard - a.shard_base;
   void *obase;
   float *lbase;
-  int ofp32;
+  float *sbase = nullptr;  // fp16 partials: inverse scale per (row, column quarter)
+  int okind;
   if (a.splits > 1) {
     const int64_t g = uniform((su * a.splits + u.split) * a.rows_total);
-    obase = a.part_o + g * kDv;
+    if (a.part_f16) {
+      okind = kOutFp16;
+      obase = reinterpret_cast<_Float16 *>(a.part_o) + g * kDv;
+      sbase = a.part_scale + g * kWaves;
+    } else {
+      okind = kOutFp32;
+      obase = reinterpret_cast<float *>(a.part_o) + g * kDv;
+    }
     lbase = a.part_lse + g;
-    ofp32 = 1;
   } else {
     const int64_t g = uniform(su * a.rows_total);
-    ofp32 = a.out_fp32;
-    obase = ofp32 ? (void *)(reinterpret_cast<float *>(a.out) + g * kDv)
-                  : (void *)(reinterpret_cast<__bf16 *>(a.out) + g * kDv);
+    okind = a.out_fp32 ? kOutFp32 : kOutBf16;
+    obase = a.out_fp32 ? (void *)(reinterpret_cast<float *>(a.out) + g * kDv)
+                       : (void *)(reinterpret_cast<__bf16 *>(a.out) + g * kDv);
     lbase = a.lse + g;
   }
   // Global output row of the group's query row r (query token r / h_q, head r % h_q).
@@ -333,8 +375,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if (row_ok) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       const int64_t gr = out_row(row_local);
-      for (int c = half * 4; c < kDv; c += 8) store_out(obase, ofp32, gr * kDv + c, z);
-      if (half == 0) lbase[gr] = -INFINITY;
+      for (int c = half * 4; c < kDv; c += 8) store_out(obase, okind, gr * kDv + c, z);
+      if (half == 0) {
+        lbase[gr] = -INFINITY;
+        if (okind == kOutFp16)
+          for (int w = 0; w < kWaves; ++w) sbase[gr * kWaves + w] = 1.f;
+      }
     }
     return;
   }
@@ -557,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if (row_ok)
       lbase[out_row(row_local)] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
-  __syncthreads();
+  lds_barrier();
   acc_result_fence(acc);
   // acc[4 rt + ct] register 4 i + j of lane (n, half) is row 32 rt + n, column
   // 128 wave + 32 ct + 8 i + 4 half + j.
@@ -565,57 +611,170 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   for (int rt = 0; rt < 4; ++rt) {
     const int r = 32 * rt + n;
     const float l = l_sh[r];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
     const bool ok = r < a.rows_per_group;
     const int64_t gr = ok ? out_row(r) : 0;
+    f32x16 v[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const f32x16 v = acc[4 * rt + ct];
-      if (ok) {
+    for (int ct = 0; ct < 4; ++ct) v[ct] = acc[4 * rt + ct];
+    float mult = l > 0.f ? 1.f / l : 0.f;
+    if (okind == kOutFp16) {
+      // Scale this row's 128 columns (the two lanes of the row hold them all)
+      // so their largest magnitude uses fp16's full range.
+      float mx = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[ct][e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float inv_scale;
+      mult *= fp16_scale(mx * mult, &inv_scale);
+      if (half == 0 && ok) sbase[gr * kWaves + wave] = inv_scale;
+    }
+    if (ok) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 o = {v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv};
-          store_out(obase, ofp32, gr * kDv + 128 * wave + 32 * ct + 8 * i + 4 * half, o);
+          const f32x4 o = {v[ct][4 * i] * mult, v[ct][4 * i + 1] * mult, v[ct][4 * i + 2] * mult,
+                           v[ct][4 * i + 3] * mult};
+          store_out(obase, okind, gr * kDv + 128 * wave + 32 * ct + 8 * i + 4 * half, o);
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// (O, lse) merge: one work-group per (group, row).  The n lse values go to LDS
-// in one cooperative load; every thread then derives the maximum and the
-// weight sum from LDS in the same fixed order and owns four consecutive columns.
-constexpr int kMergeThreads = 128;
-constexpr int kMaxMerge = 1024;
+// (O, lse) merge: one wave per (group, row), four rows per work-group.  Every
+// lane derives the maximum and the weight sum of the row's n lse values with
+// the same fixed-order wave reduction, then owns kCols consecutive columns of
+// each 64 * kCols column chunk; partials are summed in index order.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeRowsPerGroup = kMergeThreads / 64;
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = fmaxf(x, __shfl_xor(x, d));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+// Partial row `part_row`, columns c .. c + kCols - 1, as fp32 (inverse scale folded
+// into the weight for fp16 partials).
+template <bool kF16, int kCols>
+struct PartialCols {
+  float v[kCols];
+  float scale;
+};
+template <bool kF16, int kCols>
+__device__ __forceinline__ PartialCols<kF16, kCols> load_partial(const MergeArgs &a, int64_t part_row, int c) {
+  PartialCols<kF16, kCols> p;
+  if constexpr (kF16) {
+    static_assert(kCols == 8, "fp16 partials are read 16 bytes at a time");
+    p.scale = a.scale_parts[part_row * (a.d_v / 128) + c / 128];
+    // Widened one 16-bit half at a time: element access into 16-bit vector
+    // types miscompiles with this toolchain (it reused one word for both).
+    const u32x4 h = *reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const _Float16 *>(a.o_parts) + part_row * a.d_v + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p.v[2 * e] = half_bits_to_float(h[e] & 0xFFFFu);
+      p.v[2 * e + 1] = half_bits_to_float(h[e] >> 16);
+    }
+  } else {
+    p.scale = 1.f;
+    const float *src = reinterpret_cast<const float *>(a.o_parts) + part_row * a.d_v + c;
+#pragma unroll
+    for (int e = 0; e < kCols; e += 4) {
+      const f32x4 o = *reinterpret_cast<const f32x4 *>(src + e);
+      p.v[e] = o[0];
+      p.v[e + 1] = o[1];
+      p.v[e + 2] = o[2];
+      p.v[e + 3] = o[3];
+    }
+  }
+  return p;
+}
+
+template <bool kF16, int kCols>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a) {
-  __shared__ float lse_sh[kMaxMerge];
-  const int64_t r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerGroup + (threadIdx.x >> 6);
   const int g = blockIdx.y;
-  const int tid = threadIdx.x;
+  if (r >= a.rows) return;  // whole wave; no barriers below
   const float *lse = a.lse_parts + (int64_t)g * a.n * a.rows + r;
-  for (int i = tid; i < a.n; i += kMergeThreads) lse_sh[i] = lse[(int64_t)i * a.rows];
-  __syncthreads();
-  float M = -INFINITY;
-  for (int i = 0; i < a.n; ++i) M = fmaxf(M, lse_sh[i]);
-  float W = 0.f;
-  if (M != -INFINITY)
-    for (int i = 0; i < a.n; ++i) W += lse_sh[i] == -INFINITY ? 0.f : expf(lse_sh[i] - M);
+  // Maximum and weight sum over all n partials; lane j looks at partials j + 64 k.
+  float M = -INFINITY, W = 0.f, wl0 = 0.f;
+  if (a.n <= 64) {  // one load per lane
+    const float li = lane < a.n ? lse[(int64_t)lane * a.rows] : -INFINITY;
+    M = wave_max(li);
+    wl0 = (M == -INFINITY || li == -INFINITY) ? 0.f : expf(li - M);
+    W = wave_sum(wl0);
+  } else {
+    for (int i = lane; i < a.n; i += 64) M = fmaxf(M, lse[(int64_t)i * a.rows]);
+    M = wave_max(M);
+    if (M != -INFINITY)
+      for (int i = lane; i < a.n; i += 64) {
+        const float li = lse[(int64_t)i * a.rows];
+        W += li == -INFINITY ? 0.f : expf(li - M);
+      }
+    W = wave_sum(W);
+  }
   const float inv = W > 0.f ? 1.f / W : 0.f;
   const int64_t out_row = (int64_t)g * a.rows + r;
-  for (int c = tid * 4; c < a.d_v; c += kMergeThreads * 4) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < a.n; ++i) {
-      const float li = lse_sh[i];
-      if (M == -INFINITY || li == -INFINITY) continue;
-      const f32x4 o = *reinterpret_cast<const f32x4 *>(
-          a.o_parts + (((int64_t)g * a.n + i) * a.rows + r) * a.d_v + c);
-      s += expf(li - M) * o;
+  const int64_t part0 = (int64_t)g * a.n * a.rows + r;  // partial i's row: part0 + i * rows
+  // Every lane runs every column chunk (the weights below live one per lane and
+  // are read across lanes); only loads and stores are limited to real columns.
+  for (int c0 = 0; c0 < a.d_v; c0 += 64 * kCols) {
+    const int c = c0 + lane * kCols;
+    const bool cols_ok = c < a.d_v;
+    float s[kCols];
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) s[e] = 0.f;
+    // Partials in chunks of 64: lane j holds the weight of partial i0 + j, read
+    // back by every lane; sums run in index order, four partials' loads at a time.
+    for (int i0 = 0; i0 < a.n && M != -INFINITY; i0 += 64) {
+      const int cnt = min(64, a.n - i0);
+      float wl = wl0;
+      if (a.n > 64) {
+        wl = 0.f;
+        if (lane < cnt) {
+          const float li = lse[(int64_t)(i0 + lane) * a.rows];
+          wl = li == -INFINITY ? 0.f : expf(li - M);
+        }
+      }
+      if (!cols_ok) continue;
+      int i = 0;
+      for (; i + 4 <= cnt; i += 4) {
+        PartialCols<kF16, kCols> p[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p[k] = load_partial<kF16, kCols>(a, part0 + (int64_t)(i0 + i + k) * a.rows, c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wi =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i + k)) * p[k].scale;
+#pragma unroll
+          for (int e = 0; e < kCols; ++e) s[e] += wi * p[k].v[e];
+        }
+      }
+      for (; i < cnt; ++i) {
+        const PartialCols<kF16, kCols> p = load_partial<kF16, kCols>(a, part0 + (int64_t)(i0 + i) * a.rows, c);
+        const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i)) * p.scale;
+#pragma unroll
+        for (int e = 0; e < kCols; ++e) s[e] += wi * p.v[e];
+      }
     }
-    store_out(a.out, a.out_fp32, out_row * a.d_v + c, s * inv);
+    if (cols_ok) {
+#pragma unroll
+      for (int e = 0; e < kCols; e += 4)
+        store_out(a.out, a.out_fp32 ? kOutFp32 : kOutBf16, out_row * a.d_v + c + e,
+                  f32x4{s[e] * inv, s[e + 1] * inv, s[e + 2] * inv, s[e + 3] * inv});
+    }
   }
-  if (tid == 0) a.lse_out[out_row] = W > 0.f ? M + logf(W) : -INFINITY;
+  if (lane == 0) a.lse_out[out_row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
 }  // namespace
@@ -631,9 +790,15 @@ hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t strea
 }
 
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream) {
-  if (args.n > kMaxMerge) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)args.rows, (unsigned)args.groups), dim3(kMergeThreads), 0,
-                     stream, args);
+  const dim3 grid((unsigned)((args.rows + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup), (unsigned)args.groups);
+  if (args.f16) {
+    if (args.d_v % 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((merge_kernel<true, 8>), grid, dim3(kMergeThreads), 0, stream, args);
+  } else if (args.d_v % 8 == 0) {
+    hipLaunchKernelGGL((merge_kernel<false, 8>), grid, dim3(kMergeThreads), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<false, 4>), grid, dim3(kMergeThreads), 0, stream, args);
+  }
   return hipGetLastError();
 }
 

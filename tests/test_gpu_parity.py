@@ -24,6 +24,7 @@ from helpers import bf16, f64, random_rows, workload  # noqa: E402
 from latent_decode_attention_amd import mla_decode as md  # noqa: E402
 from latent_decode_attention_amd import workloads as W  # noqa: E402
 from latent_decode_attention_amd.device import upload, run  # noqa: E402
+from latent_decode_attention_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -126,20 +127,24 @@ def test_sharded_then_merge_equals_unsharded():
     assert_lse_close(mlse, rl, "merged")
 
 
-def test_merge_kernel_against_oracle():
-    g = np.random.default_rng(3)
-    n, rows = 5, 300
-    o = g.standard_normal((n, rows, 512)).astype(np.float32)
+@pytest.mark.parametrize("n,rows,d_v", [(5, 300, 512), (3, 7, 12), (70, 5, 136)])
+def test_merge_kernel_against_oracle(n, rows, d_v):
+    """Public merge of fp32 partials; d_v = 12 takes the 4-column path, n = 70
+    more partials than a wave has lanes, rows not a multiple of the rows per
+    work-group."""
+    g = np.random.default_rng(3 + n)
+    o = g.standard_normal((n, rows, d_v)).astype(np.float32)
     l = (g.standard_normal((n, rows)) * 4).astype(np.float32)
     l[1, :50] = -np.inf
-    l[:, 60] = -np.inf
+    empty = rows // 2 + 1
+    l[:, empty] = -np.inf
     ro, rl = oracle.merge(o.astype(np.float64), l.astype(np.float64))
     for dt in (torch.float32, torch.bfloat16):
         out, lse = md.mla_merge_lse(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda(), out_dtype=dt)
         torch.cuda.synchronize()
         assert_o_close(out, ro, "merge")
         assert_lse_close(lse, rl, "merge")
-    assert torch.all(out[60].float() == 0) and torch.isneginf(lse[60])
+    assert torch.all(out[empty].float() == 0) and torch.isneginf(lse[empty])
 
 
 # ---------------------------------------------------------------- exact probes
@@ -357,3 +362,36 @@ def test_full_size_split_kv_config_sampled():
     ro, rl = oracle.dense(w, rows=rows)
     assert_o_close(merged.reshape(-1, 512)[idx], ro, "merged")
     assert_lse_close(mlse.reshape(-1)[idx], rl, "merged")
+
+
+def test_fp16_partials_keep_bf16_accuracy_at_large_magnitudes():
+    """bf16-output calls store split-KV partials as fp16 with a power-of-two scale
+    per (row, 128-column quarter).  With the cache scaled by 4 (exact in bf16)
+    outputs reach |O| > 4 and every sequence is split into many partitions.
+
+    At this scale the absolute 1e-2 bar does not apply: the bf16 softmax weights
+    (relative step 2^-9 each; O is normalised by their own sum) move O by up to
+    2^-9 * sum_p w_p |v_p - O| <= 2^-8 * max|V|.  So both paths are held to that
+    bound against the oracle, and the fp16-partial path (bf16 out) is held to the
+    fp32-partial path (fp32 out) within the partials' 2^-11 relative step of the
+    largest value a partial can hold (max|V|) plus the final bf16 rounding."""
+    w = W.make_workload("scaled_cache_b2_h128_s2048", 2, 1, 128, [2048, 1300], 64, seed=41)
+    w.kv = f32_to_bf16_bits(bf16_bits_to_f32(w.kv) * np.float32(4.0)).reshape(w.kv.shape)
+    d = upload(w)
+    pl = md.mla_plan_query(md.make_problem(d.q, d.kv, d.block_table, d.seq_lens, w.scale, w.max_seq_len))
+    assert pl["splits"] > 8
+    ob, lb = run(d, out_dtype=torch.bfloat16)
+    of, lf = run(d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.dense(w)
+    assert np.abs(ro).max() > 4.0
+    assert_lse_close(lb, rl, "bf16 out")
+    assert_lse_close(lf, rl, "fp32 out")
+    v_max = float(np.nanmax(np.abs(bf16_bits_to_f32(w.kv[..., :512]))))  # spare blocks hold NaN
+    g_b = ob.float().cpu().numpy().reshape(ro.shape).astype(np.float64)
+    g_f = of.float().cpu().numpy().reshape(ro.shape).astype(np.float64)
+    p_bound = 2.0 ** -8 * v_max + 1e-4
+    assert np.abs(g_f - ro).max() <= p_bound
+    assert np.all(np.abs(g_b - ro) <= p_bound + 2.0 ** -11 * v_max + 0.5 * ulp_bf16(np.abs(ro) * 1.01))
+    agree = 2.0 ** -11 * v_max + 0.5 * ulp_bf16(np.abs(g_f) * 1.001) + 1e-6
+    assert np.all(np.abs(g_b - g_f) <= agree)
