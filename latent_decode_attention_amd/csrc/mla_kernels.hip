@@ -24,10 +24,10 @@
 //    the causal limit are zero-filled in LDS and never read from memory;
 //  * an LDS tile holds 64 rows as 9 column groups of 128 bytes (8 chunks of
 //    16 bytes): group g of row r lives at g * 8192 + r * 128.  Within a group
-//    the chunks of row r are XOR-swizzled by a key of r mod 8 so that the K
-//    reads (8 rows, same chunk) and the transposed V reads (4 rows, two
-//    neighbouring chunks) each hit 32 distinct banks, and so that each lane's
-//    direct loads come from only two rows.
+//    the chunks of row r are XOR-swizzled by a key of (r / 2) mod 8 chosen so
+//    that both the K reads (16 rows, one chunk each, per 16 lanes) and the
+//    transposed V reads (4 rows x 4 chunks per 32 lanes) touch every LDS bank
+//    exactly once.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -118,9 +118,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Chunk key of tile row r: 0, 4, 1, 5, 2, 6, 3, 7 for (r / 2) mod 8.  Even rows
+// and odd rows sit in opposite halves of the 64 banks, so a K read (rows
+// r0..r0+15 at one logical chunk) is conflict-free when the 8 even rows, and the
+// 8 odd rows, have distinct keys; a transposed V read (rows r0..r0+3, chunks
+// 4 j .. 4 j + 3) when rows r and r + 2 differ in key bit 2.  The key repeats
+// every 16 rows, so sub-block and k-block offsets keep it.
 __device__ __forceinline__ int chunk_key(int row) {
-  const int x = row & 7;
-  return ((x & 3) << 1) | (x >> 2);
+  const int m = (row >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
 }
 
 __device__ __forceinline__ int shard_len(int S, int N, int I, int r) {
@@ -245,36 +251,40 @@ __device__ __forceinline__ void dma16(const char *src, unsigned lds_base) {
 // 16w + 8 (j / 9) + l / 8 and stored position l % 8 of it.  Rows nobody
 // attends (row index -1) are copied from the zero row.
 struct TileCopy {
-  int row[2];       // this lane's cache row in each 8-row block (-1: the zero row)
-  int chunk;        // byte offset of this lane's 16-byte chunk within a column group
-  unsigned lds[2];  // wave-uniform LDS address of each 8-row block, group 0
+  const char *src[2];  // this lane's 16 source bytes in each 8-row block, group 0
+  unsigned lds[2];     // wave-uniform LDS address of each 8-row block, group 0
 };
 
 __device__ __forceinline__ TileCopy prepare_copy(Smem &sm, const DecodeArgs &a, int buf, int wave, int lane,
                                                  int tile_row) {
   TileCopy c;
-  const int sub = lane >> 3;
-  c.chunk = ((lane & 7) ^ chunk_key(sub)) * 16;
+  // Cheap per-lane constants, recomputed on every call (opaque copy of the lane)
+  // rather than hoisted out of the tile loop and held in registers.
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const int sub = l >> 3;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    c.row[k] = __shfl(tile_row, 16 * wave + 8 * k + sub);
+    const int chunk = ((l & 7) ^ chunk_key(8 * k + sub)) * 16;
+    const int row = __shfl(tile_row, 16 * wave + 8 * k + sub);
+    // Both candidates are formed and one is selected, so no branch or exec-mask
+    // change is needed (unattended tokens read the zero row).
+    const char *row_src = reinterpret_cast<const char *>(a.kv) + (int64_t)max(row, 0) * kRowBytes;
+    c.src[k] = (row < 0 ? reinterpret_cast<const char *>(kZeroRow) : row_src) + chunk;
     const unsigned blk = (unsigned)(uintptr_t)(&sm.tile[buf][(16 * wave + 8 * k) * 128]);
     c.lds[k] = __builtin_amdgcn_readfirstlane(blk);
   }
   return c;
 }
 
-__device__ __forceinline__ void copy_step(const DecodeArgs &a, const TileCopy &c, int j) {
+__device__ __forceinline__ void copy_step(const TileCopy &c, int j) {
   const int k = j / kGroups, g = j % kGroups;
-  const int row = c.row[k];
-  const char *base = row < 0 ? reinterpret_cast<const char *>(kZeroRow)
-                             : reinterpret_cast<const char *>(a.kv) + (int64_t)row * kRowBytes;
-  dma16(base + c.chunk + g * 128, c.lds[k] + g * kGroupBytes);
+  dma16(c.src[k] + g * 128, c.lds[k] + g * kGroupBytes);
 }
 
-__device__ __forceinline__ void copy_all(const DecodeArgs &a, const TileCopy &c) {
+__device__ __forceinline__ void copy_all(const TileCopy &c) {
 #pragma unroll
-  for (int j = 0; j < kCopySteps; ++j) copy_step(a, c, j);
+  for (int j = 0; j < kCopySteps; ++j) copy_step(c, j);
 }
 
 // acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 with (1, 1)).
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     const int b0 = raw_block(a, u, p0);
     bn1 = raw_block(a, u, pn1);
     const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
-    copy_all(a, prepare_copy(sm, a, 0, wave, lane, row0));
+    copy_all(prepare_copy(sm, a, 0, wave, lane, row0));
     mask_cur = tile_mask(a, u, p0, row0);
   };
   start_pass();
@@ -423,13 +433,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // 2 st + half of row n (+32 rows for the second sub-block): with the row's
   // XOR key that is column group st / 4 (an immediate) plus the per-lane base
   // with its chunk bits flipped by 2 (st % 4).  V reads of k-block kb and
-  // column tile ct: rows 16 kb + 4 half + (lane & 15) / 4 (+8), columns
-  // 128 wave + 32 ct + 16 ((lane >> 4) & 1) + 4 (lane & 3): column group
-  // 2 wave + ct / 2 plus the per-lane base with chunk bit 2 flipped for odd ct.
+  // column tile ct: rows 16 kb + 4 half + (lane & 15) / 4 (second read: + 8),
+  // columns 128 wave + 32 ct + 16 ((lane >> 4) & 1) + 4 (lane & 3): column
+  // group 2 wave + ct / 2 plus the per-lane base (one per read, the two rows
+  // having different keys) with chunk bit 2 flipped for odd ct.
   const int k_base = n * 128 + (((half ^ chunk_key(n)) & 7) << 4);
   const int v_row = 4 * half + ((lane & 15) >> 2);
   const int v_lc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int v_base = 2 * wave * kGroupBytes + v_row * 128 + (((v_lc ^ chunk_key(v_row)) & 7) << 4) + 8 * (lane & 1);
+  const int v_base8 =
+      2 * wave * kGroupBytes + (v_row + 8) * 128 + (((v_lc ^ chunk_key(v_row + 8)) & 7) << 4) + 8 * (lane & 1);
   const bf16x8 zero8 = {};
   unsigned ones2 = 0x3F803F80u;  // (1.0, 1.0) in bf16, kept in a register
   asm volatile("" : "+v"(ones2));
@@ -467,7 +480,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const int pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
       // The copy of tile t+1 is spread over this tile's score loops, one
       // instruction every fourth MFMA step, so it issues in the MFMAs' shadow.
-      const bool copy_next = t + 1 < ntiles;
+      // After the last tile every row is -1 and the copy moves zero rows into
+      // the idle buffer (drained after the loop), which avoids a branch per copy.
       const TileCopy next_copy = prepare_copy(sm, a, cur ^ 1, wave, lane, row1);
 
       const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
@@ -486,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
         for (int st = 0; st < kQkSteps; ++st) {
           const int step = sb * kQkSteps + st;
-          if ((step & 3) == 0 && copy_next) copy_step(a, next_copy, step >> 2);
+          if ((step & 3) == 0) copy_step(next_copy, step >> 2);
           if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
           if (st == 0)
             mfma_vgpr_first(s, kr[0], qr[0]);
@@ -556,9 +570,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         for (int rt = 0; rt < 4; ++rt) pr[rt] = sm.p[kb >> 1][rt][kb & 1][lane];
         i16x4 vr[2][2];
         auto v_read = [&](int ct, i16x4 *dst) {
-          const char LDS_AS *va0 = tb + (v_base ^ ((ct & 1) << 6)) + (ct >> 1) * kGroupBytes + 16 * kb * 128;
-          dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)va0);
-          dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(va0 + 8 * 128));
+          const int grp = (ct >> 1) * kGroupBytes + 16 * kb * 128;
+          dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(tb + (v_base ^ ((ct & 1) << 6)) + grp));
+          dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(tb + (v_base8 ^ ((ct & 1) << 6)) + grp));
         };
         v_read(0, vr[0]);
 #pragma unroll
@@ -580,7 +594,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     }
 
     // ---- recompute vote: did any row outgrow its reference?  (The tile
-    // buffers are free once every wave is past the last tile.)
+    // buffers are free once every wave is past the last tile and the zero-row
+    // copies issued by the last tile have landed.)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     int *vote = reinterpret_cast<int *>(sm.tile[0]);
     if (lane == 0) vote[wave] = __any(overflow) ? 1 : 0;
