@@ -168,7 +168,8 @@ const char *mla_status_string(mla_status_t status);
  */
 typedef struct {
   int32_t q_per_group;    /* query tokens handled together by one work-group */
-  int32_t rows_per_group; /* q_per_group * h_q */
+  int32_t rows_per_group; /* query rows per work-group: q_per_group * h_q, or 64 when
+                             h_q > 64 (each query token's heads in 64-head chunks) */
   int32_t units;          /* (sequence, query group, shard) work units */
   int32_t splits;         /* KV partitions per unit */
   int32_t chunk;          /* tokens per partition (multiple of the 64-token tile) */
@@ -180,6 +181,18 @@ typedef struct {
 mla_status_t mla_plan_query(const mla_problem_t *problem, int32_t num_shards,
                             int32_t interleave, int32_t shard_id, int32_t top_k,
                             int64_t index_stride_q, int32_t num_cus, mla_plan_t *plan);
+
+/*
+ * Work-group shape control.  Each decode work-group handles up to 128 or up to
+ * 64 query rows; by default (rows = 0) the plan picks per problem: 64 when the
+ * rows fit in 64 anyway, when 64-row groups need no KV partitions while
+ * 128-row groups would, or when 128-row partitions would be 4 tiles or fewer.
+ * rows = 64 or 128 forces that shape for every later plan and decode call in
+ * the process (results agree within rounding; the softmax weights are
+ * normalised per row either way).  Not synchronised with calls in flight on
+ * other threads.  Returns MLA_ERR_BAD_SHAPE for any other value.
+ */
+mla_status_t mla_set_group_rows(int32_t rows);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@
 // DCP exchange ("RFC: MsModeling 支持 Decode Context Parallel 仿真", §1.1,
 // §2.1.4.3).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -26,8 +27,12 @@ constexpr int kMaxShards = 4096;
 constexpr int kMaxTopK = 65536;
 constexpr int kMaxMergeParts = 1024;
 
+// Rows per work-group forced by mla_set_group_rows (0: chosen per problem).
+std::atomic<int> g_group_rows{0};
+
 struct Plan {
-  int q_per_group, rows_per_group, q_groups, shard_units;
+  int q_per_group, rows_per_group, q_groups, head_chunks, shard_units;
+  int kernel_rows;  // 128 or 64
   int units, splits, chunk, stream_len;
   int64_t grid;
   size_t ws_o, ws_lse, ws_scale, ws_total;
@@ -49,7 +54,7 @@ mla_status_t check_problem(const mla_problem_t *p) {
   if (p->B < 1 || p->Q < 1 || p->h_q < 1 || p->num_blocks < 1 || p->max_blocks < 1 ||
       p->max_seq_len < 1)
     return MLA_ERR_BAD_SHAPE;
-  if (p->Q > 16 || p->h_q > kMaxRowsPerGroup) return MLA_ERR_UNSUPPORTED;
+  if (p->Q > 16 || p->h_q > kMaxHeads) return MLA_ERR_UNSUPPORTED;
   if (p->block_size < 1 || p->block_size > 4096 || (p->block_size & (p->block_size - 1)))
     return MLA_ERR_BAD_SHAPE;
   if ((int64_t)p->num_blocks * p->block_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
@@ -71,13 +76,6 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
     if (interleave < 1 || shard_id < -1 || shard_id >= num_shards) return MLA_ERR_BAD_SHAPE;
   }
   if (num_cus < 1) num_cus = kDefaultCus;
-  const int rows_all = p->Q * p->h_q;
-  const bool shared_list = !sparse || idx_stride_q == 0 || p->Q == 1;
-  pl->q_per_group =
-      (shared_list && rows_all <= kMaxRowsPerGroup && p->Q <= kMaxQPerGroup) ? p->Q : 1;
-  pl->rows_per_group = pl->q_per_group * p->h_q;
-  pl->q_groups = p->Q / pl->q_per_group;
-  pl->shard_units = (num_shards > 1 && shard_id < 0) ? num_shards : 1;
   int64_t L;
   if (sparse) {
     L = top_k;
@@ -89,19 +87,56 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   } else {
     L = p->max_seq_len;
   }
-  pl->stream_len = (int)L;
-  const int64_t units = (int64_t)p->B * pl->q_groups * pl->shard_units;
-  if (units > INT32_MAX) return MLA_ERR_BAD_SHAPE;
-  pl->units = (int)units;
   const int64_t tiles = (L + kTile - 1) / kTile;
-  int64_t splits = 1;
-  if (units < num_cus && tiles > 1) splits = std::min<int64_t>((num_cus + units - 1) / units, tiles);
-  const int64_t tiles_per_split = tiles > 0 ? (tiles + splits - 1) / splits : 1;
-  splits = tiles > 0 ? (tiles + tiles_per_split - 1) / tiles_per_split : 1;
-  pl->splits = (int)splits;
-  pl->chunk = (int)(tiles_per_split * kTile);
-  pl->grid = units * splits;
-  if (pl->grid > INT32_MAX) return MLA_ERR_BAD_SHAPE;
+  const bool shared_list = !sparse || idx_stride_q == 0 || p->Q == 1;
+  const int shard_units = (num_shards > 1 && shard_id < 0) ? num_shards : 1;
+
+  // Query groups of up to R rows (R = 128 or 64) that share one token stream:
+  // heads beyond R are cut into R-head chunks of one query token; fewer heads
+  // are packed as whole query tokens (the most that divide Q and fit, when
+  // every token of the group attends the same index list).  The token stream
+  // of each (sequence, group, shard) unit is then cut into partitions until
+  // the launch fills the device.
+  auto layout = [&](int R, Plan *o) -> bool {
+    o->kernel_rows = R;
+    o->head_chunks = (p->h_q + R - 1) / R;
+    o->q_per_group = 1;
+    if (o->head_chunks == 1 && shared_list)
+      for (int d = std::min(p->Q, kMaxQPerGroup); d > 1; --d)
+        if (p->Q % d == 0 && d * p->h_q <= R) {
+          o->q_per_group = d;
+          break;
+        }
+    o->rows_per_group = o->head_chunks > 1 ? R : o->q_per_group * p->h_q;
+    o->q_groups = p->Q / o->q_per_group * o->head_chunks;
+    o->shard_units = shard_units;
+    o->stream_len = (int)L;
+    const int64_t units = (int64_t)p->B * o->q_groups * shard_units;
+    if (units > INT32_MAX) return false;
+    o->units = (int)units;
+    int64_t splits = 1;
+    if (units < num_cus && tiles > 1) splits = std::min<int64_t>((num_cus + units - 1) / units, tiles);
+    const int64_t tiles_per_split = tiles > 0 ? (tiles + splits - 1) / splits : 1;
+    splits = tiles > 0 ? (tiles + tiles_per_split - 1) / tiles_per_split : 1;
+    o->splits = (int)splits;
+    o->chunk = (int)(tiles_per_split * kTile);
+    o->grid = units * splits;
+    return o->grid <= INT32_MAX;
+  };
+  // 128-row groups halve the per-tile fixed costs relative to the matrix
+  // work; 64-row groups halve the partial results and the query rows each
+  // work-group loads.  Take 64 when the groups fit in 64 rows anyway, when
+  // they avoid partials altogether, or when the partitions are short enough
+  // (at most 4 tiles) that the per-call costs dominate.
+  Plan wide, narrow;
+  if (!layout(128, &wide) || !layout(64, &narrow)) return MLA_ERR_BAD_SHAPE;
+  const int64_t wide_tiles = wide.chunk / kTile;
+  const int forced = g_group_rows.load(std::memory_order_relaxed);
+  const bool use_narrow =
+      forced ? forced == 64
+             : wide.rows_per_group <= 64 || (narrow.splits == 1 && wide.splits > 1) || wide_tiles <= 4;
+  *pl = use_narrow ? narrow : wide;
+  const int64_t splits = pl->splits;
   const int64_t rows_total = (int64_t)p->B * p->Q * p->h_q;
   if (splits > 1) {
     // Sized for fp32 partials; bf16-output calls store fp16 partials in the
@@ -162,6 +197,8 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
   a.q_per_group = pl.q_per_group;
   a.rows_per_group = pl.rows_per_group;
   a.q_groups = pl.q_groups;
+  a.head_chunks = pl.head_chunks;
+  a.kernel_rows = pl.kernel_rows;
   a.splits = pl.splits;
   a.chunk = pl.chunk;
   a.rows_total = (int64_t)p->B * p->Q * p->h_q;
@@ -281,6 +318,12 @@ const char *mla_status_string(mla_status_t s) {
     case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable gfx950 device";
   }
   return "unknown mla_status_t";
+}
+
+mla_status_t mla_set_group_rows(int32_t rows) {
+  if (rows != 0 && rows != 64 && rows != 128) return MLA_ERR_BAD_SHAPE;
+  g_group_rows.store(rows, std::memory_order_relaxed);
+  return MLA_OK;
 }
 
 mla_status_t mla_plan_query(const mla_problem_t *problem, int32_t num_shards, int32_t interleave,

@@ -12,7 +12,8 @@ namespace mla {
 constexpr int kDqk = 576;        // latent row width: kv_lora_rank 512 + RoPE 64
 constexpr int kDv = 512;         // value columns = leading kv_lora_rank columns
 constexpr int kTile = 64;        // tokens staged in LDS per pipeline step
-constexpr int kMaxRowsPerGroup = 128;  // query rows (q token x head) per work-group
+constexpr int kMaxRowsPerGroup = 128;  // query rows (q token x head) per work-group: 128 or 64
+constexpr int kMaxHeads = 128;         // query heads per token
 constexpr int kMaxQPerGroup = 4;       // query tokens per work-group (attended masks kept per token)
 
 // Everything one decode launch needs.  Passed by value as the kernel argument.
@@ -30,6 +31,8 @@ struct DecodeArgs {
   float scale_log2;            // scale * log2(e): scores are kept in base-2 units
   int32_t num_shards, interleave, shard_base, shard_units;
   int32_t q_per_group, rows_per_group, q_groups;
+  int32_t head_chunks;         // groups per query token (heads cut into chunks of rows_per_group), else 1
+  int32_t kernel_rows;         // work-group shape: 128 or 64 query rows (>= rows_per_group)
   int32_t splits, chunk;
   int64_t rows_total;          // B * Q * h_q
   // final results (splits == 1)

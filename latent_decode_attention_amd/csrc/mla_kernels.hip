@@ -1,19 +1,20 @@
 // MLA decode attention kernels for gfx950 (MI355X).
 //
-// One work-group (4 waves x 64 lanes) owns one (sequence, query-token group,
-// shard, KV partition) unit of up to 128 query rows (query token x head) and
-// streams that unit's latent rows through LDS in 64-token tiles.  Every query
-// head dots the same latent row (h_kv = 1 for MLA: "RFC: MsModeling 支持
-// Decode Context Parallel 仿真", §2.1.4 symbol table), so per tile the work is
-// two dense contractions on the bf16 matrix cores:
-//   scores  S^T[token, row] = K_tile[64 x 576] . Q^T[576 x 32]    wave w: rows 32w..32w+31
-//   output  O^T[col, row]  += V_tile^T[128 x 64] . P^T[64 x 128]  wave w: cols 128w..128w+127
-// with V_tile = the first 512 columns of the same LDS rows.  Each wave turns
-// its scores into softmax weights P and publishes them in LDS; every wave then
-// multiplies all 128 rows' weights against its own quarter of the value
-// columns, so each transposed V operand read from LDS feeds four MFMAs.  The KV
-// partitions of a unit and the DCP shards are combined by the log-sum-exp merge
-// the DCP page describes (§1.1, §2.1.4.3).
+// One work-group (4 waves x 64 lanes) owns one (sequence, query group, shard,
+// KV partition) unit of up to 64 query rows (query token x head: the heads of
+// one token, or whole tokens when heads are few) and streams that unit's latent
+// rows through LDS in 64-token tiles.  Every query head dots the same latent row
+// (h_kv = 1 for MLA: "RFC: MsModeling 支持 Decode Context Parallel 仿真", §2.1.4
+// symbol table), so per tile the work is two dense contractions on the bf16
+// matrix cores:
+//   scores  S^T[token, row] = K[32 x 576] . Q^T[576 x 32]   wave w: rows 32 (w & 1).., tokens 32 (w >> 1)..
+//   output  O^T[col, row]  += V^T[128 x 64] . P^T[64 x 64]  wave w: cols 128 w..128 w + 127
+// with V = the first 512 columns of the same LDS rows.  Each wave turns its
+// scores into softmax weights P and publishes them in LDS; every wave then
+// multiplies all 64 rows' weights against its own quarter of the value
+// columns.  Two work-groups cover the 128 heads of a DeepSeek-style query
+// token; the KV partitions of a unit and the DCP shards are combined by the
+// log-sum-exp merge the DCP page describes (§1.1, §2.1.4.3).
 //
 // Data movement:
 //  * every wave derives the positions, block-table rows (§2.1.4.1, table A) and
@@ -56,7 +57,6 @@ constexpr int kQkSteps = kDqk / 16;            // 36 k-steps of the 32x32x16 MFM
 constexpr int kGroups = kChunks / 8;           // 9 column groups of 128 bytes
 constexpr int kGroupBytes = kTile * 128;       // 8192
 constexpr int kCopySteps = 2 * kGroups;        // direct-load instructions per wave per tile
-constexpr int kAccTiles = 16;                  // 4 row tiles x 4 column tiles of 32 x 32
 // How far (base 2) a score may exceed its row's reference maximum before the
 // unit is recomputed with a higher reference: p <= 2^60 keeps sum(p) * |v| far
 // inside the fp32 range for any realistic row.
@@ -64,20 +64,26 @@ constexpr float kHeadroomLog2 = 60.0f;
 constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unconstrained
 
 static_assert(kTile == 16 * kWaves, "each wave copies 16 rows of a tile");
-static_assert(kMaxRowsPerGroup == 32 * kWaves, "each wave owns 32 query rows");
-static_assert(kQkSteps * 2 == 4 * kCopySteps, "one copy step every fourth score step");
+static_assert(kWaves == 4, "four waves: four row tiles, or two row tiles x two token halves");
 constexpr int kKAhead = 3;  // K operand reads in flight ahead of the MFMA that uses them
 
 // Source of the bytes copied for tokens that no query row attends, so that a
 // tile never holds stale or poisoned rows and the copies need no per-lane branch.
 __device__ __attribute__((aligned(256))) const unsigned kZeroRow[kRowBytes / 4] = {};
 
+template <int kRows>
 struct __attribute__((aligned(16))) Smem {
   char tile[2][kTileBytes];  // double-buffered latent rows
-  // Softmax weights as MFMA B operands: [sub-block][owner wave][k-block][lane].
-  bf16x8 p[2][kWaves][2][64];
+  // Softmax weights as MFMA B operands: [k-block][row tile][lane].
+  bf16x8 p[4][kRows / 32][64];
 };
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one work-group");
+template <>
+struct __attribute__((aligned(16))) Smem<64> {
+  char tile[2][kTileBytes];
+  bf16x8 p[4][2][64];
+  float mx[kWaves][32];  // first-tile row maxima exchanged by the two waves of a row tile
+};
+static_assert(sizeof(Smem<128>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024, "LDS budget of one work-group");
 
 // ---- Matrix-core helpers.  The 256 output accumulators of a lane fill the
 // whole AGPR file, so the MFMAs are written as inline asm with register-class
@@ -103,10 +109,11 @@ __device__ __forceinline__ void mfma_result_fence(f32x16 &d) {
 }
 // VALU-written VGPRs -> MFMA operand reads.
 __device__ __forceinline__ void operand_fence(bf16x8 &a) { asm volatile("s_nop 3" : "+v"(a)); }
+template <int kTiles>
 __device__ __forceinline__ void acc_result_fence(f32x16 *acc) {
   asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < kAccTiles; ++i) asm volatile("" : "+a"(acc[i]));
+  for (int i = 0; i < kTiles; ++i) asm volatile("" : "+a"(acc[i]));
 }
 
 // Work-group barrier that orders LDS accesses only.  __syncthreads() also
@@ -142,6 +149,8 @@ enum StreamMode { kDenseStream = 0, kShardStream = 1, kSparseStream = 2 };
 
 struct Unit {
   int b, q0, shard, split;
+  int h0, rows;   // first head and number of query rows of the group
+  int64_t row0;   // flattened (query token, head) row of the group's row 0
   int S, i0, i1;
   int64_t idx_base;
   const int32_t *bt;  // this sequence's block-table row
@@ -172,7 +181,10 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
   id /= a.q_groups;
   const int su = (int)(id % a.shard_units);
   u.b = (int)(id / a.shard_units);
-  u.q0 = qg * a.q_per_group;
+  u.q0 = (qg / a.head_chunks) * a.q_per_group;
+  u.h0 = (qg % a.head_chunks) * a.rows_per_group;
+  u.rows = min(a.rows_per_group, a.q_per_group * a.h_q - u.h0);
+  u.row0 = uniform(((int64_t)u.b * a.Q + u.q0) * a.h_q + u.h0);
   u.shard = a.shard_base + su;
   u.S = uniform(a.seq_lens[u.b]);
   int L;
@@ -255,7 +267,7 @@ struct TileCopy {
   unsigned lds[2];     // wave-uniform LDS address of each 8-row block, group 0
 };
 
-__device__ __forceinline__ TileCopy prepare_copy(Smem &sm, const DecodeArgs &a, int buf, int wave, int lane,
+__device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArgs &a, int wave, int lane,
                                                  int tile_row) {
   TileCopy c;
   // Cheap per-lane constants, recomputed on every call (opaque copy of the lane)
@@ -271,7 +283,7 @@ __device__ __forceinline__ TileCopy prepare_copy(Smem &sm, const DecodeArgs &a, 
     // change is needed (unattended tokens read the zero row).
     const char *row_src = reinterpret_cast<const char *>(a.kv) + (int64_t)max(row, 0) * kRowBytes;
     c.src[k] = (row < 0 ? reinterpret_cast<const char *>(kZeroRow) : row_src) + chunk;
-    const unsigned blk = (unsigned)(uintptr_t)(&sm.tile[buf][(16 * wave + 8 * k) * 128]);
+    const unsigned blk = (unsigned)(uintptr_t)(tile_buf + (16 * wave + 8 * k) * 128);
     c.lds[k] = __builtin_amdgcn_readfirstlane(blk);
   }
   return c;
@@ -336,12 +348,24 @@ __device__ __forceinline__ float fp16_scale(float vmax, float *inv) {
   return __builtin_bit_cast(float, (unsigned)(14 - e + 127) << 23);
 }
 
-template <int kMode>
+// kRows = 128: wave w scores rows 32 w.. against both 32-token halves of each
+// tile in turn (two sub-blocks) and owns those rows' softmax state outright.
+// kRows = 64: wave w scores row tile w & 1 against token half w >> 1 only, so
+// the two waves of a row tile (w, w ^ 2) agree on the rows' reference maximum
+// at the first tile and combine their sums at the end.
+template <int kMode, int kRows>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
-  __shared__ Smem sm;
+  constexpr int kRowTiles = kRows / 32;
+  constexpr int kAccTiles = 4 * kRowTiles;  // row tiles x 4 column tiles of 32 x 32
+  constexpr int kSubBlocks = kRows / 64;    // 32-token score blocks per wave per tile
+  constexpr int kCopyEvery = kSubBlocks * kQkSteps / kCopySteps;  // score steps per copy step
+  static_assert(kCopyEvery * kCopySteps == kSubBlocks * kQkSteps, "copies spread evenly over the scores");
+  __shared__ Smem<kRows> sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, half = lane >> 5;
+  const int rh = kRows == 128 ? wave : (wave & 1);  // the wave's row tile for the scores
+  const int th = kRows == 128 ? 0 : (wave >> 1);    // its token half (64 rows)
 
   const Unit u = decode_unit<kMode>(a);
   const int ntiles = u.i1 > u.i0 ? (u.i1 - u.i0 + kTile - 1) / kTile : 0;
@@ -370,19 +394,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
                        : (void *)(reinterpret_cast<__bf16 *>(a.out) + g * kDv);
     lbase = a.lse + g;
   }
-  // Global output row of the group's query row r (query token r / h_q, head r % h_q).
-  auto out_row = [&](int r) -> int64_t {
-    const int ql = r / a.h_q;
-    return ((int64_t)u.b * a.Q + u.q0 + ql) * a.h_q + (r - ql * a.h_q);
-  };
+  // Global row (query token x head, flattened) of the group's row r.
+  auto out_row = [&](int r) -> int64_t { return u.row0 + r; };
 
-  // The wave's 32 query rows for the scores; lanes n and n + 32 share a row.
-  const int row_local = wave * 32 + n;
-  const bool row_ok = row_local < a.rows_per_group;
+  const int row_local = 32 * rh + n;
+  const bool row_ok = row_local < u.rows;
 
   if (ntiles == 0) {
-    // Nothing attended: O = 0, lse = -inf.
-    if (row_ok) {
+    // Nothing attended: O = 0, lse = -inf (written by the token-half-0 waves).
+    if (th == 0 && row_ok) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       const int64_t gr = out_row(row_local);
       for (int c = half * 4; c < kDv; c += 8) store_out(obase, okind, gr * kDv + c, z);
@@ -394,7 +414,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     }
     return;
   }
-  const int q_local = row_ok ? row_local / a.h_q : 0;
+  // Query token of the row within the group (heads of one token are contiguous).
+  const int q_local = row_ok ? (u.h0 + row_local) / a.h_q : 0;
 
   // ---- Start of a pass: the memory chain positions -> block ids -> rows ->
   // copy of tile 0, with the positions of tiles 0..2 and the block ids of
@@ -412,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     const int b0 = raw_block(a, u, p0);
     bn1 = raw_block(a, u, pn1);
     const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
-    copy_all(prepare_copy(sm, a, 0, wave, lane, row0));
+    copy_all(prepare_copy(sm.tile[0], a, wave, lane, row0));
     mask_cur = tile_mask(a, u, p0, row0);
   };
   start_pass();
@@ -430,14 +451,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   }
 
   // Per-lane LDS byte offsets within a tile.  K step st reads logical chunk
-  // 2 st + half of row n (+32 rows for the second sub-block): with the row's
-  // XOR key that is column group st / 4 (an immediate) plus the per-lane base
-  // with its chunk bits flipped by 2 (st % 4).  V reads of k-block kb and
-  // column tile ct: rows 16 kb + 4 half + (lane & 15) / 4 (second read: + 8),
-  // columns 128 wave + 32 ct + 16 ((lane >> 4) & 1) + 4 (lane & 3): column
-  // group 2 wave + ct / 2 plus the per-lane base (one per read, the two rows
-  // having different keys) with chunk bit 2 flipped for odd ct.
-  const int k_base = n * 128 + (((half ^ chunk_key(n)) & 7) << 4);
+  // 2 st + half of row 32 th + n: with the row's XOR key that is column group
+  // st / 4 (an immediate) plus the per-lane base with its chunk bits flipped by
+  // 2 (st % 4).  V reads of k-block kb and column tile ct: rows
+  // 16 kb + 4 half + (lane & 15) / 4 (second read: + 8), columns
+  // 128 wave + 32 ct + 16 ((lane >> 4) & 1) + 4 (lane & 3): column group
+  // 2 wave + ct / 2 plus the per-lane base (one per read, the two rows having
+  // different keys) with chunk bit 2 flipped for odd ct.
+  const int k_base = th * 32 * 128 + n * 128 + (((half ^ chunk_key(n)) & 7) << 4);
   const int v_row = 4 * half + ((lane & 15) >> 2);
   const int v_lc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int v_base = 2 * wave * kGroupBytes + v_row * 128 + (((v_lc ^ chunk_key(v_row)) & 7) << 4) + 8 * (lane & 1);
@@ -448,15 +469,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   asm volatile("" : "+v"(ones2));
 
   // Softmax bookkeeping for this wave's 32 rows, base-2 units.  m_ref is the
-  // row's reference maximum: set from the first sub-block in which the row
-  // attends anything, and only ever raised by a recompute pass.  p = 2^(x - m_ref)
-  // may exceed 1 by up to 2^kHeadroomLog2, which fp32 accumulators and bf16
-  // operands carry without loss, so the accumulators are never rescaled.
+  // row's reference maximum, raised only by a recompute pass (to the largest
+  // score seen).  128 rows: set from the first sub-block in which the row
+  // attends anything.  64 rows: common to the row's two waves, the larger of
+  // their first-tile maxima; a row first attending later forces a recompute.
+  // p = 2^(x - m_ref) may exceed 1 by up to 2^kHeadroomLog2, which fp32
+  // accumulators and bf16 operands carry without loss, so the accumulators are
+  // never rescaled; a score beyond that headroom sends the unit through a
+  // recompute pass.
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;  // largest score seen so far
   float l_run = 0.f;         // this lane's share of sum(p), for lse
   float l_rnd = 0.f;         // the same sum over p as rounded to bf16, for O
   f32x16 acc[kAccTiles];     // acc[4 rt + ct]: rows 32 rt.., columns 128 wave + 32 ct..
+  bool first_pass = true;
 
   for (;;) {
     bf16x8 z = zero8;
@@ -478,56 +504,61 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // top (after its wait), so no wait on them falls inside this tile.
       const int bn2 = raw_block(a, u, pn2);
       const int pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
-      // The copy of tile t+1 is spread over this tile's score loops, one
-      // instruction every fourth MFMA step, so it issues in the MFMAs' shadow.
+      // The copy of tile t+1 is spread over this tile's score loop, one
+      // instruction every second MFMA step, so it issues in the MFMAs' shadow.
       // After the last tile every row is -1 and the copy moves zero rows into
       // the idle buffer (drained after the loop), which avoids a branch per copy.
-      const TileCopy next_copy = prepare_copy(sm, a, cur ^ 1, wave, lane, row1);
+      const TileCopy next_copy = prepare_copy(sm.tile[cur ^ 1], a, wave, lane, row1);
 
       const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
 
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        // ---- scores S^T = K . Q^T for the sub-block's 32 tokens.  The operand
-        // of step st + kKAhead is read while step st multiplies.
+      for (int sb = 0; sb < kSubBlocks; ++sb) {
+        // Token half of this score block: the sub-block (128 rows) or the
+        // wave's own half (64 rows, where th is already in k_base).
+        const int tok = kRows == 128 ? sb : th;
+        // ---- scores S^T = K . Q^T for 32 tokens and the wave's 32 rows.  The
+        // operand of step st + kKAhead is read while step st multiplies.
         f32x16 s;
-        bf16x8 kr[kKAhead + 1];
-        auto k_read = [&](int st) {
-          return *(const bf16x8 LDS_AS *)(tb + (k_base ^ ((st & 3) << 5)) + (st >> 2) * kGroupBytes + sb * 32 * 128);
-        };
+        {
+          bf16x8 kr[kKAhead + 1];
+          auto k_read = [&](int st) {
+            return *(const bf16x8 LDS_AS *)(tb + (k_base ^ ((st & 3) << 5)) + (st >> 2) * kGroupBytes +
+                                             (kRows == 128 ? sb * 32 * 128 : 0));
+          };
 #pragma unroll
-        for (int st = 0; st < kKAhead; ++st) kr[st] = k_read(st);
+          for (int st = 0; st < kKAhead; ++st) kr[st] = k_read(st);
 #pragma unroll
-        for (int st = 0; st < kQkSteps; ++st) {
-          const int step = sb * kQkSteps + st;
-          if ((step & 3) == 0) copy_step(next_copy, step >> 2);
-          if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
-          if (st == 0)
-            mfma_vgpr_first(s, kr[0], qr[0]);
-          else
-            mfma_vgpr(s, kr[st % (kKAhead + 1)], qr[st]);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int st = 0; st < kQkSteps; ++st) {
+            const int step = sb * kQkSteps + st;
+            if (step % kCopyEvery == 0) copy_step(next_copy, step / kCopyEvery);
+            if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
+            if (st == 0)
+              mfma_vgpr_first(s, kr[0], qr[0]);
+            else
+              mfma_vgpr(s, kr[st % (kKAhead + 1)], qr[st]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         mfma_result_fence(s);
 
         // ---- mask, weights.  Register r of lane (n, half) is token
-        // 8 (r / 4) + 4 half + r % 4 of the sub-block.  Scores stay unscaled
+        // 32 tok + 8 (r / 4) + 4 half + r % 4 of the tile.  Scores stay unscaled
         // until the exponent (the scale is positive, so the maximum commutes).
         float x[16];
         if (mask_cur.full) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] = s[r];
         } else {
-          // This lane's tokens are 4 half + {0..3} (+8 i, +32 sb): shift once so
-          // every bit test uses a compile-time position.
+          // Shift once so every bit test uses a compile-time position.
           unsigned long long msk = mask_cur.m[0];
 #pragma unroll
           for (int qq = 1; qq < kMaxQPerGroup; ++qq)
             if (q_local == qq) msk = mask_cur.m[qq];
-          msk = half ? msk >> 4 : msk;
+          msk >>= 32 * tok + 4 * half;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int bit = 32 * sb + 8 * (r >> 2) + (r & 3);
+            const int bit = 8 * (r >> 2) + (r & 3);
             x[r] = ((msk >> bit) & 1ull) ? s[r] : -INFINITY;
           }
         }
@@ -536,7 +567,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         for (int r = 0; r < 16; ++r) smax = fmaxf(smax, x[r]);
         smax = fmaxf(smax, __shfl_xor(smax, 32)) * a.scale_log2;
         m_seen = fmaxf(m_seen, smax);
-        if (m_ref == -INFINITY) m_ref = smax;  // first scores of this row: acc is still 0
+        if constexpr (kRows == 128) {
+          if (m_ref == -INFINITY) m_ref = smax;  // first scores of this row: acc is still 0
+        } else if (first_pass && t == 0) {
+          // The row's reference: the larger first-tile maximum of its two waves.
+          if (half == 0) sm.mx[wave][n] = smax;
+          lds_barrier();
+          m_ref = fmaxf(sm.mx[rh][n], sm.mx[rh + 2][n]);
+        }
         overflow |= smax > m_ref + kHeadroomLog2;
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
@@ -553,21 +591,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           // used, so it stays an exact convex combination of the V rows.
 #pragma unroll
           for (int e = 0; e < 4; ++e) l_rnd = sum_bf16_pair(l_rnd, w[e], ones2);
-          // P^T operand of k-block 2 sb + k: lane (row n, half) holds tokens
-          // 16 k + 8 (e / 4) + 4 half + e % 4 of the sub-block.
-          sm.p[sb][wave][k][lane] = __builtin_bit_cast(bf16x8, w);
+          // P^T operand of k-block 2 tok + k, row tile rh: lane (row n, half)
+          // holds tokens 16 (2 tok + k) + 8 (e / 4) + 4 half + e % 4.
+          sm.p[2 * tok + k][rh][lane] = __builtin_bit_cast(bf16x8, w);
         }
       }
       __syncthreads();  // every wave's weights for this tile are in LDS
 
-      // ---- O^T += V^T . P^T for this wave's 128 columns and all 128 rows.
+      // ---- O^T += V^T . P^T for this wave's 128 columns and all 64 rows.
       // The transposed LDS read gives lane (m, half) V[token(half, e)][col m]
       // for e = 0..3 (rows +0..3) and e = 4..7 (rows +8..11): the k order of P^T.
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        bf16x8 pr[4];
+        bf16x8 pr[kRowTiles];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) pr[rt] = sm.p[kb >> 1][rt][kb & 1][lane];
+        for (int rt = 0; rt < kRowTiles; ++rt) pr[rt] = sm.p[kb][rt][lane];
         i16x4 vr[2][2];
         auto v_read = [&](int ct, i16x4 *dst) {
           const int grp = (ct >> 1) * kGroupBytes + 16 * kb * 128;
@@ -582,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
               bf16x8, __builtin_shufflevector(vr[ct & 1][0], vr[ct & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
           operand_fence(va);
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[rt]);
+          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[rt]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -593,41 +631,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       pn2 = pn3;
     }
 
-    // ---- recompute vote: did any row outgrow its reference?  (The tile
-    // buffers are free once every wave is past the last tile and the zero-row
-    // copies issued by the last tile have landed.)
+    // ---- recompute vote: did any row outgrow its reference?  With 64 rows
+    // each wave also publishes its rows' largest score for the row's other
+    // wave.  (The tile buffers are free once every wave is past the last tile
+    // and the zero-row copies issued by the last tile have landed.)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     int *vote = reinterpret_cast<int *>(sm.tile[0]);
+    float *seen = reinterpret_cast<float *>(sm.tile[0] + 64);
     if (lane == 0) vote[wave] = __any(overflow) ? 1 : 0;
+    if (kRows == 64 && half == 0) seen[wave * 32 + n] = m_seen;
     __syncthreads();
     const bool redo = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
-    __syncthreads();
+    const float m_all = kRows == 64 ? fmaxf(seen[rh * 32 + n], seen[(rh + 2) * 32 + n]) : m_seen;
+    __syncthreads();  // read before the next pass copies into the buffer
     if (!redo) break;
     // Redo the unit with every reference raised to the largest score seen.
-    m_ref = m_seen;
+    m_ref = m_all;
+    first_pass = false;
     start_pass();
   }
 
   // ---- finalize.  Each wave's outputs cover all rows, so the rounded row
-  // sums go through LDS (the tile buffers are free now).
-  float *l_sh = reinterpret_cast<float *>(sm.tile[0]);
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float l_rnd_tot = l_rnd + __shfl_xor(l_rnd, 32);
+  // sums go through LDS (the tile buffers are free now); with 64 rows the sums
+  // of a row's two waves are added there too.
+  float *l_sh = reinterpret_cast<float *>(sm.tile[0]);  // [sum kind][wave][32]
+  const float l_run_w = l_run + __shfl_xor(l_run, 32);
+  const float l_rnd_w = l_rnd + __shfl_xor(l_rnd, 32);
   if (half == 0) {
-    l_sh[row_local] = l_rnd_tot;
-    if (row_ok)
-      lbase[out_row(row_local)] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    l_sh[wave * 32 + n] = l_run_w;
+    l_sh[kWaves * 32 + wave * 32 + n] = l_rnd_w;
   }
   lds_barrier();
-  acc_result_fence(acc);
+  // Row sum of kind k (0: exact, 1: rounded) of row 32 r_t + n.
+  auto row_sum = [&](int k, int r_t) -> float {
+    const float *b = l_sh + k * kWaves * 32 + n;
+    return kRows == 128 ? b[r_t * 32] : b[r_t * 32] + b[(r_t + 2) * 32];
+  };
+  if (th == 0 && half == 0 && row_ok) {
+    const float l_tot = row_sum(0, rh);
+    lbase[out_row(row_local)] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+  acc_result_fence<kAccTiles>(acc);
   // acc[4 rt + ct] register 4 i + j of lane (n, half) is row 32 rt + n, column
   // 128 wave + 32 ct + 8 i + 4 half + j.
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < kRowTiles; ++rt) {
     const int r = 32 * rt + n;
-    const float l = l_sh[r];
-    const bool ok = r < a.rows_per_group;
+    const float l = row_sum(1, rt);
+    const bool ok = r < u.rows;
     const int64_t gr = ok ? out_row(r) : 0;
     f32x16 v[4];
 #pragma unroll
@@ -796,12 +848,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
-  if (args.sparse)
-    hipLaunchKernelGGL(decode_kernel<kSparseStream>, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
-  else if (args.num_shards > 1)
-    hipLaunchKernelGGL(decode_kernel<kShardStream>, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL(decode_kernel<kDenseStream>, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+  const dim3 g((unsigned)grid), b(kThreads);
+  const bool wide = args.kernel_rows == 128;
+  if (args.sparse) {
+    if (wide) hipLaunchKernelGGL((decode_kernel<kSparseStream, 128>), g, b, 0, stream, args);
+    else hipLaunchKernelGGL((decode_kernel<kSparseStream, 64>), g, b, 0, stream, args);
+  } else if (args.num_shards > 1) {
+    if (wide) hipLaunchKernelGGL((decode_kernel<kShardStream, 128>), g, b, 0, stream, args);
+    else hipLaunchKernelGGL((decode_kernel<kShardStream, 64>), g, b, 0, stream, args);
+  } else {
+    if (wide) hipLaunchKernelGGL((decode_kernel<kDenseStream, 128>), g, b, 0, stream, args);
+    else hipLaunchKernelGGL((decode_kernel<kDenseStream, 64>), g, b, 0, stream, args);
+  }
   return hipGetLastError();
 }
 

@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_plan_query.argtypes = [P, i32, i32, i32, i32, i64, i32, ctypes.POINTER(Plan)]
     lib.mla_plan_query.restype = ctypes.c_int
+    lib.mla_set_group_rows.argtypes = [i32]
+    lib.mla_set_group_rows.restype = ctypes.c_int
     return lib
 
 
@@ -132,6 +134,11 @@ def mla_plan_query(problem: Problem, num_shards: int = 1, interleave: int = 1, s
     _check(lib.mla_plan_query(ctypes.byref(problem), num_shards, interleave, shard_id, top_k,
                               index_stride_q, num_cus, ctypes.byref(plan)))
     return plan.as_dict()
+
+
+def mla_set_group_rows(rows: int) -> None:
+    """Force 64- or 128-row decode work-groups (0: chosen per problem)."""
+    _check(lib.mla_set_group_rows(rows))
 
 
 def _workspace(problem, num_shards, shard_id, top_k, workspace, device):

@@ -101,19 +101,31 @@ def plan(p, **kw):
 
 
 def test_plan_fills_the_device_and_covers_every_tile():
-    # sparse B=32 h=128 top_k=2048: 32 units -> 8 partitions of 256 tokens
+    # sparse B=32 h=128 top_k=2048: 128-row groups would leave partitions of 4
+    # tiles, so 64-row groups: 2 head chunks x 32 sequences = 64 units -> 4
+    # partitions of 512 tokens
     pl = plan(problem(B=32, max_seq_len=32768, max_blocks=512), top_k=2048)
-    assert (pl["units"], pl["splits"], pl["chunk"], pl["grid"]) == (32, 8, 256, 256)
-    assert pl["workspace_bytes"] >= 8 * 32 * 128 * 512 * 4
-    # dense B=32 S=4096
+    assert (pl["q_per_group"], pl["rows_per_group"]) == (1, 64)
+    assert (pl["units"], pl["splits"], pl["chunk"], pl["grid"]) == (64, 4, 512, 256)
+    assert pl["workspace_bytes"] >= 4 * 32 * 128 * 512 * 4
+    # dense B=32 S=4096: 128-row groups, 8 partitions of 8 tiles
     pl = plan(problem(B=32, max_seq_len=4096, max_blocks=64))
+    assert pl["rows_per_group"] == 128
     assert (pl["splits"], pl["chunk"], pl["grid"]) == (8, 512, 256)
     # enough units: no partitions, no scratch
     pl = plan(problem(B=512, max_seq_len=4096, max_blocks=64))
     assert pl["splits"] == 1 and pl["workspace_bytes"] == 0
-    # MTP: Q=2 x h=64 share one work-group
+    # MTP: Q=2 x h=64 as one 64-row group per query token needs no partitions
+    # (two tokens per 128-row group would); Q=4 x h=16 share one group
     pl = plan(problem(B=128, Q=2, h_q=64, max_seq_len=65536, max_blocks=1024), top_k=2048)
-    assert pl["q_per_group"] == 2 and pl["rows_per_group"] == 128 and pl["units"] == 128
+    assert pl["q_per_group"] == 1 and pl["rows_per_group"] == 64 and pl["units"] == 256
+    pl = plan(problem(B=8, Q=4, h_q=16, max_seq_len=4096, max_blocks=64))
+    assert pl["q_per_group"] == 4 and pl["rows_per_group"] == 64 and pl["units"] == 8
+    pl = plan(problem(B=8, Q=4, h_q=32, max_seq_len=4096, max_blocks=64))
+    assert pl["q_per_group"] == 2 and pl["rows_per_group"] == 64 and pl["units"] == 16
+    # h_q = 96: a 64-head chunk and a 32-head chunk per query token
+    pl = plan(problem(B=8, Q=2, h_q=96, max_seq_len=4096, max_blocks=64))
+    assert pl["q_per_group"] == 1 and pl["rows_per_group"] == 64 and pl["units"] == 32
     # per-token index lists split the query tokens
     pl = plan(problem(B=128, Q=2, h_q=64, max_seq_len=65536, max_blocks=1024), top_k=2048,
               index_stride_q=2048)
@@ -130,10 +142,29 @@ def test_plan_shards_cover_their_positions(S, N, I):
         assert pl["stream_len"] == want
         assert pl["splits"] * pl["chunk"] >= want and pl["chunk"] % 64 == 0
         assert (pl["splits"] - 1) * pl["chunk"] < max(want, 1)
-        units = 8 * (N if r < 0 else 1)
+        chunks = 128 // pl["rows_per_group"]  # 64-row groups: two head chunks of h_q = 128
+        units = 8 * chunks * (N if r < 0 else 1)
         assert pl["grid"] == units * pl["splits"]
 
 
 def test_plan_rejects_sparse_shards():
     assert lib.mla_plan_query(ctypes.byref(problem()), 2, 64, -1, 2048, 0, 256,
                               ctypes.byref(md.Plan())) == 3
+
+
+def test_forced_group_rows_override_the_plan_and_reject_other_values():
+    dense = problem(B=32, max_seq_len=4096, max_blocks=64)
+    sparse = problem(B=32, max_seq_len=32768, max_blocks=512)
+    try:
+        md.mla_set_group_rows(64)
+        pl = plan(dense)
+        assert (pl["rows_per_group"], pl["units"], pl["splits"], pl["chunk"]) == (64, 64, 4, 1024)
+        md.mla_set_group_rows(128)
+        pl = plan(sparse, top_k=2048)
+        assert (pl["rows_per_group"], pl["units"], pl["splits"], pl["chunk"]) == (128, 32, 8, 256)
+        for bad in (-1, 1, 32, 96, 256):
+            assert lib.mla_set_group_rows(bad) == 2
+        assert plan(sparse, top_k=2048)["rows_per_group"] == 128  # a rejected value changes nothing
+    finally:
+        md.mla_set_group_rows(0)
+    assert plan(dense)["rows_per_group"] == 128 and plan(sparse, top_k=2048)["rows_per_group"] == 64

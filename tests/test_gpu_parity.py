@@ -29,6 +29,14 @@ from latent_decode_attention_amd.workloads import bf16_bits_to_f32, f32_to_bf16_
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=[64, 128], ids=["rows64", "rows128"])
+def group_rows(request):
+    """Every case runs with 64-row and with 128-row decode work-groups."""
+    md.mla_set_group_rows(request.param)
+    yield request.param
+    md.mla_set_group_rows(0)
+
+
 def ulp_bf16(x):
     ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
@@ -309,6 +317,42 @@ def test_large_score_jump_takes_the_restart_path():
     ro, rl = oracle.dense(w)
     assert_o_close(out, ro, "restart")
     assert_lse_close(lse, rl, "restart")
+
+
+@pytest.mark.parametrize("jump_at", [40, 100, 500])
+def test_score_jump_in_any_tile_matches_the_oracle(jump_at):
+    # 64 sequences of 600 tokens, so each work-group's partition spans 2-3
+    # tiles.  The first tile peaks at 8 nats; one later token of every sequence
+    # scores 64 nats (80 base-2 units above): in the first tile's other token
+    # half (64-row groups take the reference from both halves), in the next
+    # tile, or in a later partition's second tile (both shapes recompute).
+    rng = np.random.default_rng(123 + jump_at)
+    S, B = 600, 64
+    rows = random_rows(rng, S, std=0.05)
+    q = np.zeros((B, 1, 64, W.D_QK), dtype=np.uint16)
+    q[..., 512] = bf16(64.0)
+    rows[:, 512] = bf16(0.0)
+    rows[10, 512] = bf16(1.0)
+    rows[jump_at, 512] = bf16(8.0)
+    w = workload(q, [rows] * B, block_size=64, scale=0.125, seed=6)
+    out, lse = run(upload(w), out_dtype=torch.float32)
+    ro, rl = oracle.dense(w)
+    assert_o_close(out, ro, f"jump at {jump_at}")
+    assert_lse_close(lse, rl, f"jump at {jump_at}")
+
+
+def test_rows_attending_nothing_in_the_first_tile():
+    # 64 sequences with 512-entry lists (partitions of 2-4 tiles).  Sequence 0's
+    # list starts with a whole tile of -1 padding and its second tile is half
+    # padding, so its rows see their first scores after the first tile.
+    w = W.make_workload("late_first", 64, 1, 128, [3000] + [2000] * 63, 64, seed=141, top_k=512)
+    w.indices = w.indices.copy()
+    w.indices[:64] = -1
+    w.indices[64:96] = -1
+    out, lse = run(upload(w), out_dtype=torch.float32)
+    ro, rl = oracle.sparse(w)
+    assert_o_close(out, ro, "late first")
+    assert_lse_close(lse, rl, "late first")
 
 
 def test_empty_sequences_and_fully_masked_rows():
