@@ -422,33 +422,46 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // tiles 0 and 1 each fetched in one round trip.  Leaves the masks of tile 0
   // and the raw lookups of tiles 1 and 2 for the tile loop.  (The opaque lane
   // copy keeps this per-pass work from being hoisted and held in registers.)
+  // `between` runs after the positions and `after_blocks` after the block ids
+  // are issued: the first pass loads the query rows there, so each wait of
+  // the chain leaves the query loads issued after it in flight.
   TileMask mask_cur;
   int pn1, bn1, pn2;
-  auto start_pass = [&]() {
+  auto start_pass = [&](auto between, auto after_blocks) {
     int plane = lane;
     asm volatile("" : "+v"(plane));
     const int p0 = raw_position<kMode>(a, u, u.i0 + plane);
     pn1 = raw_position<kMode>(a, u, u.i0 + kTile + plane);
     pn2 = raw_position<kMode>(a, u, u.i0 + 2 * kTile + plane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the load order: each wait below
+    between();                          // then leaves the later loads in flight
+    __builtin_amdgcn_sched_barrier(0);
     const int b0 = raw_block(a, u, p0);
     bn1 = raw_block(a, u, pn1);
+    __builtin_amdgcn_sched_barrier(0);
+    after_blocks();
+    __builtin_amdgcn_sched_barrier(0);
     const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
     copy_all(prepare_copy(sm.tile[0], a, wave, lane, row0));
     mask_cur = tile_mask(a, u, p0, row0);
   };
-  start_pass();
 
   // Query rows in registers: lane (n, half) holds q[row][16 st + 8 half + 0..7], the
-  // B operand of the 32x32x16 MFMA for k-step st.  Loaded after the copy of
-  // tile 0 is under way, so the two share the memory pipeline; the first
-  // tile's wait covers both.  Rows past the group's end load the group's first
-  // row instead (no branch around the loads); their outputs are never stored.
+  // B operand of the 32x32x16 MFMA for k-step st, loaded in two halves inside
+  // the first pass's lookup chain; the first tile's wait covers them.  Rows
+  // past the group's end load the group's first row instead (no branch around
+  // the loads); their outputs are never stored.
   bf16x8 qr[kQkSteps];
-  {
-    const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + out_row(row_ok ? row_local : 0) * kDqk);
+  const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + out_row(row_ok ? row_local : 0) * kDqk);
+  start_pass(
+      [&]() {
 #pragma unroll
-    for (int st = 0; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
-  }
+        for (int st = 0; st < kQkSteps / 2; ++st) qr[st] = qp[2 * st + half];
+      },
+      [&]() {
+#pragma unroll
+        for (int st = kQkSteps / 2; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
+      });
 
   // Per-lane LDS byte offsets within a tile.  K step st reads logical chunk
   // 2 st + half of row 32 th + n: with the row's XOR key that is column group
@@ -649,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // Redo the unit with every reference raised to the largest score seen.
     m_ref = m_all;
     first_pass = false;
-    start_pass();
+    start_pass([]() {}, []() {});
   }
 
   // ---- finalize.  Each wave's outputs cover all rows, so the rounded row
