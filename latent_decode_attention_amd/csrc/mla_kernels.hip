@@ -267,8 +267,19 @@ struct TileCopy {
   unsigned lds[2];     // wave-uniform LDS address of each 8-row block, group 0
 };
 
-__device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArgs &a, int wave, int lane,
-                                                 int tile_row) {
+// The cache rows of the two tokens lane l copies: tokens 16 w + 8 k + l / 8 of
+// the tile, fetched from the lanes that derived them (lane = token).
+struct CopyRows {
+  int row[2];
+};
+__device__ __forceinline__ CopyRows copy_rows(int tile_row, int wave, int lane) {
+  CopyRows r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) r.row[k] = __shfl(tile_row, 16 * wave + 8 * k + (lane >> 3));
+  return r;
+}
+__device__ __forceinline__ TileCopy copy_from_rows(char *tile_buf, const DecodeArgs &a, int wave, int lane,
+                                                   const CopyRows &r) {
   TileCopy c;
   // Cheap per-lane constants, recomputed on every call (opaque copy of the lane)
   // rather than hoisted out of the tile loop and held in registers.
@@ -278,7 +289,7 @@ __device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArg
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int chunk = ((l & 7) ^ chunk_key(8 * k + sub)) * 16;
-    const int row = __shfl(tile_row, 16 * wave + 8 * k + sub);
+    const int row = r.row[k];
     // Both candidates are formed and one is selected, so no branch or exec-mask
     // change is needed (unattended tokens read the zero row).
     const char *row_src = reinterpret_cast<const char *>(a.kv) + (int64_t)max(row, 0) * kRowBytes;
@@ -287,6 +298,10 @@ __device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArg
     c.lds[k] = __builtin_amdgcn_readfirstlane(blk);
   }
   return c;
+}
+__device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArgs &a, int wave, int lane,
+                                                 int tile_row) {
+  return copy_from_rows(tile_buf, a, wave, lane, copy_rows(tile_row, wave, lane));
 }
 
 __device__ __forceinline__ void copy_step(const TileCopy &c, int j) {
@@ -358,8 +373,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   constexpr int kRowTiles = kRows / 32;
   constexpr int kAccTiles = 4 * kRowTiles;  // row tiles x 4 column tiles of 32 x 32
   constexpr int kSubBlocks = kRows / 64;    // 32-token score blocks per wave per tile
-  constexpr int kCopyEvery = kSubBlocks * kQkSteps / kCopySteps;  // score steps per copy step
-  static_assert(kCopyEvery * kCopySteps == kSubBlocks * kQkSteps, "copies spread evenly over the scores");
+  constexpr int kPvSteps = 16;               // (k-block, column tile) steps of P.V
+  constexpr int kCopyFirst = 8;              // first step that copies (after the tile's set-up work)
+  constexpr int kCopyEvery = (kSubBlocks * kQkSteps + kPvSteps - kCopyFirst) / kCopySteps;
+  static_assert(kCopyFirst + kCopyEvery * (kCopySteps - 1) < kSubBlocks * kQkSteps + kPvSteps,
+                "the copy of the next tile is issued within the tile");
   __shared__ Smem<kRows> sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -510,18 +528,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const int cur = t & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t have landed
       __syncthreads();                       // ... every wave's; tile t-1's P and V are consumed
-      // Rows and masks of tile t+1 from lookups that landed with the wait above.
-      const int row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
-      const TileMask mask1 = tile_mask(a, u, pn1, row1);
-      // Raw lookups two and three tiles ahead, examined only at the next tile's
-      // top (after its wait), so no wait on them falls inside this tile.
-      const int bn2 = raw_block(a, u, pn2);
-      const int pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
-      // The copy of tile t+1 is spread over this tile's score loop, one
-      // instruction every second MFMA step, so it issues in the MFMAs' shadow.
-      // After the last tile every row is -1 and the copy moves zero rows into
-      // the idle buffer (drained after the loop), which avoids a branch per copy.
-      const TileCopy next_copy = prepare_copy(sm.tile[cur ^ 1], a, wave, lane, row1);
+      // Tile t+1's rows and masks (from lookups that landed with the wait
+      // above), its copy addresses, and the raw lookups two and three tiles
+      // ahead are worked out during the first score steps, in the MFMAs'
+      // shadow; the lookups are examined only at the next tile's top (after its
+      // wait), so no wait on them falls inside this tile.  The copy of tile t+1
+      // then issues one instruction every kCopyEvery steps from step
+      // kCopyFirst on, through the scores and into the P.V steps.  After the
+      // last tile every row is -1 and the copy moves zero rows into the idle
+      // buffer (drained after the loop), which avoids a branch per copy.
+      int row1 = -1, bn2 = 0, pn3 = 0;
+      TileMask mask1;
+      CopyRows crow;
+      TileCopy next_copy;
+      auto tile_step_work = [&](int step) {
+        if (step == 0) {
+          bn2 = raw_block(a, u, pn2);
+          pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
+        }
+        if (step == 1) row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
+        if (step == 2) crow = copy_rows(row1, wave, lane);
+        if (step == 3) mask1 = tile_mask(a, u, pn1, row1);
+        if (step == 5) next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);
+        if (step >= kCopyFirst && (step - kCopyFirst) % kCopyEvery == 0 &&
+            (step - kCopyFirst) / kCopyEvery < kCopySteps)
+          copy_step(next_copy, (step - kCopyFirst) / kCopyEvery);
+      };
 
       const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
 
@@ -543,8 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int st = 0; st < kKAhead; ++st) kr[st] = k_read(st);
 #pragma unroll
           for (int st = 0; st < kQkSteps; ++st) {
-            const int step = sb * kQkSteps + st;
-            if (step % kCopyEvery == 0) copy_step(next_copy, step / kCopyEvery);
+            tile_step_work(sb * kQkSteps + st);
             if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
             if (st == 0)
               mfma_vgpr_first(s, kr[0], qr[0]);
@@ -611,29 +642,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       }
       __syncthreads();  // every wave's weights for this tile are in LDS
 
-      // ---- O^T += V^T . P^T for this wave's 128 columns and all 64 rows.
-      // The transposed LDS read gives lane (m, half) V[token(half, e)][col m]
-      // for e = 0..3 (rows +0..3) and e = 4..7 (rows +8..11): the k order of P^T.
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        bf16x8 pr[kRowTiles];
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) pr[rt] = sm.p[kb][rt][lane];
-        i16x4 vr[2][2];
-        auto v_read = [&](int ct, i16x4 *dst) {
+      // ---- O^T += V^T . P^T for this wave's 128 columns and all rows, in
+      // (k-block kb, column tile ct) steps.  The transposed LDS read gives lane
+      // (m, half) V[token(half, e)][col m] for e = 0..3 (rows +0..3) and
+      // e = 4..7 (rows +8..11): the k order of P^T.  V operands are read
+      // kVAhead steps ahead and each k-block's weights two steps before it.
+      {
+        constexpr int kVAhead = kRows == 128 ? 1 : 2;  // 4 (128 rows) or 2 MFMAs per V operand
+        i16x4 vr[kVAhead + 1][2];
+        bf16x8 pr[2][kRowTiles];
+        auto v_read = [&](int j, i16x4 *dst) {
+          const int kb = j >> 2, ct = j & 3;
           const int grp = (ct >> 1) * kGroupBytes + 16 * kb * 128;
           dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(tb + (v_base ^ ((ct & 1) << 6)) + grp));
           dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(tb + (v_base8 ^ ((ct & 1) << 6)) + grp));
         };
-        v_read(0, vr[0]);
+        auto p_read = [&](int kb, bf16x8 *dst) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          if (ct + 1 < 4) v_read(ct + 1, vr[(ct + 1) & 1]);
-          bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(vr[ct & 1][0], vr[ct & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          operand_fence(va);
+          for (int rt = 0; rt < kRowTiles; ++rt) dst[rt] = sm.p[kb][rt][lane];
+        };
+        p_read(0, pr[0]);
 #pragma unroll
-          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[rt]);
+        for (int j = 0; j < kVAhead; ++j) v_read(j, vr[j]);
+#pragma unroll
+        for (int j = 0; j < kPvSteps; ++j) {
+          const int kb = j >> 2, ct = j & 3;
+          tile_step_work(kSubBlocks * kQkSteps + j);
+          if (ct == 2 && kb + 1 < 4) p_read(kb + 1, pr[(kb + 1) & 1]);
+          if (j + kVAhead < kPvSteps) v_read(j + kVAhead, vr[(j + kVAhead) % (kVAhead + 1)]);
+          const i16x4 *v = vr[j % (kVAhead + 1)];
+          // Straight from the LDS reads into consecutive registers: no VALU
+          // write precedes the MFMA's operand read.
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[kb & 1][rt]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
