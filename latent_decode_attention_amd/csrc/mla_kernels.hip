@@ -900,6 +900,86 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
   if (lane == 0) a.lse_out[out_row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
+// Merge of a few partials of 512 columns (the decode's own split-KV merge):
+// one wave per row, 8 columns per lane.  Every load (the row's n lse values at
+// one address per wave, this lane's columns of each partial and their scale)
+// is issued before any is used, so the row costs one memory round trip; every
+// lane then forms the maximum, the weights and their sum itself, in index
+// order, with no cross-lane traffic.
+constexpr int kMergeSmallN = 8;
+template <bool kF16>
+__global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerGroup + (threadIdx.x >> 6);
+  const int g = blockIdx.y;
+  if (r >= a.rows) return;
+  const int c = lane * 8;
+  const int64_t part0 = (int64_t)g * a.n * a.rows + r;  // partial i's row: part0 + i * rows
+  // Raw loads, unconditional (partials past n re-read partial n - 1 and are
+  // masked below), so they issue back to back.  Each loaded vector is split
+  // into scalars at once: element reads from arrays of vectors miscompile with
+  // this toolchain (only element 0 survived).
+  float li[kMergeSmallN], sc[kMergeSmallN];
+  unsigned raw[kMergeSmallN][kF16 ? 4 : 8];
+#pragma unroll
+  for (int i = 0; i < kMergeSmallN; ++i) {
+    const int64_t pr = part0 + (int64_t)min(i, a.n - 1) * a.rows;
+    li[i] = a.lse_parts[pr];
+    if constexpr (kF16) {
+      sc[i] = a.scale_parts[pr * 4 + (c >> 7)];
+      const u32x4 h = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const _Float16 *>(a.o_parts) + pr * 512 + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[i][e] = h[e];
+    } else {
+      sc[i] = 1.f;
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.o_parts) + pr * 512 + c);
+      const u32x4 lo = src[0], hi = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        raw[i][e] = lo[e];
+        raw[i][4 + e] = hi[e];
+      }
+    }
+  }
+  // No branches below (a branch lets the compiler sink the loads after it):
+  // partials past n, and partials with lse = -inf, get weight 0.
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeSmallN; ++i) M = fmaxf(M, i < a.n ? li[i] : -INFINITY);
+  float W = 0.f;
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMergeSmallN; ++i) {
+    const float wi = (i < a.n && li[i] != -INFINITY) ? expf(li[i] - M) : 0.f;
+    W += wi;
+    const float ws = wi * sc[i];
+    float v[8];
+    if constexpr (kF16) {
+      // Widened one 16-bit half at a time (element access into 16-bit vector
+      // types miscompiles with this toolchain).
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = half_bits_to_float(raw[i][e] & 0xFFFFu);
+        v[2 * e + 1] = half_bits_to_float(raw[i][e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(float, raw[i][e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += ws * v[e];
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  const int64_t out_row = (int64_t)g * a.rows + r;
+#pragma unroll
+  for (int e = 0; e < 8; e += 4)
+    store_out(a.out, a.out_fp32 ? kOutFp32 : kOutBf16, out_row * a.d_v + c + e,
+              f32x4{s[e] * inv, s[e + 1] * inv, s[e + 2] * inv, s[e + 3] * inv});
+  if (lane == 0) a.lse_out[out_row] = W > 0.f ? M + logf(W) : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
@@ -920,7 +1000,12 @@ hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t strea
 
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream) {
   const dim3 grid((unsigned)((args.rows + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup), (unsigned)args.groups);
-  if (args.f16) {
+  if (args.d_v == 512 && args.n <= kMergeSmallN) {
+    if (args.f16)
+      hipLaunchKernelGGL((merge_small_kernel<true>), grid, dim3(kMergeThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL((merge_small_kernel<false>), grid, dim3(kMergeThreads), 0, stream, args);
+  } else if (args.f16) {
     if (args.d_v % 128) return hipErrorInvalidValue;
     hipLaunchKernelGGL((merge_kernel<true, 8>), grid, dim3(kMergeThreads), 0, stream, args);
   } else if (args.d_v % 8 == 0) {
