@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -729,7 +731,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   }
   acc_result_fence<kAccTiles>(acc);
   // acc[4 rt + ct] register 4 i + j of lane (n, half) is row 32 rt + n, column
-  // 128 wave + 32 ct + 8 i + 4 half + j.
+  // 128 wave + 32 ct + 8 i + 4 half + j.  Each 32-row tile of the wave's
+  // columns is normalised, converted and staged row-major in the wave's slice
+  // of the idle second tile buffer, then stored back 16 bytes per lane as
+  // whole row segments (4 rows of 256 bytes, or 2 of 512, per instruction)
+  // rather than as 16-byte pieces of 32 rows.
+  char *stage = sm.tile[1] + wave * 32 * (512 + 16);
+  auto store_tile = [&](int rt, auto esz_c) {
+    constexpr int kEsz = decltype(esz_c)::value;  // output element bytes
+    constexpr int kSeg = 128 * kEsz;              // one row's bytes of this wave's columns
+    constexpr int kStride = kSeg + 16;            // padded LDS row pitch
+    constexpr int kLanesPerRow = kSeg / 16;
+    constexpr int kRowsPerStep = 64 / kLanesPerRow;
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPerStep; ++k) {
+      const int row = k * kRowsPerStep + lane / kLanesPerRow;
+      const int byte = (lane % kLanesPerRow) * 16;
+      const u32x4 d = *reinterpret_cast<const u32x4 *>(stage + row * kStride + byte);
+      const int rl = 32 * rt + row;
+      if (rl < u.rows)
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(obase) + (out_row(rl) * kDv + 128 * wave) * kEsz + byte) = d;
+    }
+  };
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
     const int r = 32 * rt + n;
@@ -753,16 +776,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       mult *= fp16_scale(mx * mult, &inv_scale);
       if (half == 0 && ok) sbase[gr * kWaves + wave] = inv_scale;
     }
-    if (ok) {
+    const bool wide_out = okind == kOutFp32;
+    const int pitch = wide_out ? 512 + 16 : 256 + 16;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 o = {v[ct][4 * i] * mult, v[ct][4 * i + 1] * mult, v[ct][4 * i + 2] * mult,
-                           v[ct][4 * i + 3] * mult};
-          store_out(obase, okind, gr * kDv + 128 * wave + 32 * ct + 8 * i + 4 * half, o);
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 o = {v[ct][4 * i] * mult, v[ct][4 * i + 1] * mult, v[ct][4 * i + 2] * mult,
+                         v[ct][4 * i + 3] * mult};
+        const int col = 32 * ct + 8 * i + 4 * half;
+        if (wide_out) {
+          *reinterpret_cast<f32x4 *>(stage + n * pitch + col * 4) = o;
+        } else {
+          const u32x2 h = okind == kOutBf16 ? u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])}
+                                            : u32x2{pack_f16(o[0], o[1]), pack_f16(o[2], o[3])};
+          *reinterpret_cast<u32x2 *>(stage + n * pitch + col * 2) = h;
         }
-    }
+      }
+    if (wide_out)
+      store_tile(rt, std::integral_constant<int, 4>());
+    else
+      store_tile(rt, std::integral_constant<int, 2>());
     __builtin_amdgcn_sched_barrier(0);
   }
 }
