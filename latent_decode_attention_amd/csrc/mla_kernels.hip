@@ -473,15 +473,45 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // the loads); their outputs are never stored.
   bf16x8 qr[kQkSteps];
   const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(a.q + out_row(row_ok ? row_local : 0) * kDqk);
-  start_pass(
-      [&]() {
+  if constexpr (kRows == 128) {
+    start_pass(
+        [&]() {
 #pragma unroll
-        for (int st = 0; st < kQkSteps / 2; ++st) qr[st] = qp[2 * st + half];
-      },
-      [&]() {
+          for (int st = 0; st < kQkSteps / 2; ++st) qr[st] = qp[2 * st + half];
+        },
+        [&]() {
 #pragma unroll
-        for (int st = kQkSteps / 2; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
-      });
+          for (int st = kQkSteps / 2; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
+        });
+  } else {
+    // The two waves of a row tile hold the same query rows: each loads half of
+    // the k-steps (token half th: k-steps 18 th..18 th+17, chosen through the
+    // address so register indices stay compile-time) and the halves meet in
+    // the idle second tile buffer, [row tile][k-step][lane] x 16 bytes =
+    // exactly one tile buffer.  Halves the query loads at the start of the
+    // kernel, which share the vector memory pipeline with its lookup chain.
+    constexpr int kHalf = kQkSteps / 2;
+    bf16x8 tq[kHalf];
+    const bf16x8 *qsrc = qp + 2 * kHalf * th;
+    start_pass(
+        [&]() {
+#pragma unroll
+          for (int j = 0; j < kHalf / 2; ++j) tq[j] = qsrc[2 * j + half];
+        },
+        [&]() {
+#pragma unroll
+          for (int j = kHalf / 2; j < kHalf; ++j) tq[j] = qsrc[2 * j + half];
+        });
+    bf16x8 *q_sh = reinterpret_cast<bf16x8 *>(sm.tile[1]) + rh * kQkSteps * 64 + lane;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the query halves (and the copy of tile 0) have landed
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j) q_sh[(kHalf * th + j) * 64] = tq[j];
+    lds_barrier();
+#pragma unroll
+    for (int st = 0; st < kQkSteps; ++st) qr[st] = q_sh[st * 64];
+    // (The first tile's top barrier orders these reads before any copy into
+    // the buffer.)
+  }
 
   // Per-lane LDS byte offsets within a tile.  K step st reads logical chunk
   // 2 st + half of row 32 th + n: with the row's XOR key that is column group
