@@ -2,13 +2,14 @@
 // C-ABI entry points declared in include/mla_decode.h.
 //
 // The planner sizes one launch to the device: a work-group per compute unit
-// (each work-group holds two 72 KiB LDS tiles, so one fits per CU).  When the
-// natural units (sequence x query group x shard) are fewer than the CUs, each
-// unit's token stream is cut into `splits` partitions of whole 64-token tiles;
-// the partitions write fp32 partial (O, lse) pairs to the caller's workspace
-// and the merge kernel combines them with the same log-sum-exp rule as the
-// DCP exchange ("RFC: MsModeling 支持 Decode Context Parallel 仿真", §1.1,
-// §2.1.4.3).
+// (each work-group holds two 72 KiB LDS tiles, so one fits per CU), each
+// covering a query group of up to 128 or up to 64 rows.  When the natural
+// units (sequence x query group x shard) are fewer than the CUs, each unit's
+// token stream is cut into `splits` partitions of whole 64-token tiles; the
+// partitions write partial (O, lse) pairs to the caller's workspace (fp16 O,
+// scaled per row quarter, for bf16 outputs) and a merge kernel combines them
+// with the same log-sum-exp rule as the DCP exchange ("RFC: MsModeling 支持
+// Decode Context Parallel 仿真", §1.1, §2.1.4.3).
 #include <algorithm>
 #include <atomic>
 #include <cmath>
