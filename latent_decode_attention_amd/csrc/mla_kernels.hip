@@ -255,8 +255,13 @@ __device__ __forceinline__ TileMask tile_mask(const DecodeArgs &a, const Unit &u
 // these kernels; the clobber records that the copy rewrites it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char *src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_base), "v"(src) : "m0");
+// M0 = lds_base + lds_off (an immediate once the copy loop is unrolled), one
+// wait state for the M0 write to reach the direct load, then the load.
+__device__ __forceinline__ void dma16(const char *src, unsigned lds_base, int lds_off) {
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(src), "i"(lds_off)
+               : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -308,7 +313,7 @@ __device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArg
 
 __device__ __forceinline__ void copy_step(const TileCopy &c, int j) {
   const int k = j / kGroups, g = j % kGroups;
-  dma16(c.src[k] + g * 128, c.lds[k] + g * kGroupBytes);
+  dma16(c.src[k] + g * 128, c.lds[k], g * kGroupBytes);
 }
 
 __device__ __forceinline__ void copy_all(const TileCopy &c) {
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   constexpr int kAccTiles = 4 * kRowTiles;  // row tiles x 4 column tiles of 32 x 32
   constexpr int kSubBlocks = kRows / 64;    // 32-token score blocks per wave per tile
   constexpr int kPvSteps = 16;               // (k-block, column tile) steps of P.V
-  constexpr int kCopyFirst = 8;              // first step that copies (after the tile's set-up work)
+  constexpr int kCopyFirst = 3;              // first step that copies (after its addresses are formed)
   constexpr int kCopyEvery = (kSubBlocks * kQkSteps + kPvSteps - kCopyFirst) / kCopySteps;
   static_assert(kCopyFirst + kCopyEvery * (kCopySteps - 1) < kSubBlocks * kQkSteps + kPvSteps,
                 "the copy of the next tile is issued within the tile");
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // shadow; the lookups are examined only at the next tile's top (after its
       // wait), so no wait on them falls inside this tile.  The copy of tile t+1
       // then issues one instruction every kCopyEvery steps from step
-      // kCopyFirst on, through the scores and into the P.V steps.  After the
+      // kCopyFirst on (its addresses come first), through the scores.  After the
       // last tile every row is -1 and the copy moves zero rows into the idle
       // buffer (drained after the loop), which avoids a branch per copy.
       int row1 = -1, bn2 = 0, pn3 = 0;
@@ -575,13 +580,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       TileCopy next_copy;
       auto tile_step_work = [&](int step) {
         if (step == 0) {
+          row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
+          crow = copy_rows(row1, wave, lane);
+        }
+        if (step == 2) next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);
+        if (step == 4) {
           bn2 = raw_block(a, u, pn2);
           pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
         }
-        if (step == 1) row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
-        if (step == 2) crow = copy_rows(row1, wave, lane);
-        if (step == 3) mask1 = tile_mask(a, u, pn1, row1);
-        if (step == 5) next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);
+        if (step == 5) mask1 = tile_mask(a, u, pn1, row1);
         if (step >= kCopyFirst && (step - kCopyFirst) % kCopyEvery == 0 &&
             (step - kCopyFirst) / kCopyEvery < kCopySteps)
           copy_step(next_copy, (step - kCopyFirst) / kCopyEvery);
