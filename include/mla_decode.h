@@ -78,6 +78,12 @@ typedef struct {
   const int32_t *seq_lens;    /* device, int32 [B], each in [Q, max_seq_len] */
   int32_t max_seq_len;        /* host-side upper bound on every seq_lens[b]; sizes the
                                  split-KV plan, >= 1 and <= max_blocks * block_size */
+  int32_t group_rows;         /* work-group shape: 0 = chosen per problem, or 64 / 128 query
+                                 rows per work-group (results agree within rounding).  By
+                                 default 64 is taken when the rows fit in 64 anyway, when
+                                 64-row groups need no KV partitions while 128-row groups
+                                 would, or when 128-row partitions would be 4 tiles or
+                                 fewer.  Any other value: MLA_ERR_BAD_SHAPE */
 } mla_problem_t;
 
 /*
@@ -181,18 +187,6 @@ typedef struct {
 mla_status_t mla_plan_query(const mla_problem_t *problem, int32_t num_shards,
                             int32_t interleave, int32_t shard_id, int32_t top_k,
                             int64_t index_stride_q, int32_t num_cus, mla_plan_t *plan);
-
-/*
- * Work-group shape control.  Each decode work-group handles up to 128 or up to
- * 64 query rows; by default (rows = 0) the plan picks per problem: 64 when the
- * rows fit in 64 anyway, when 64-row groups need no KV partitions while
- * 128-row groups would, or when 128-row partitions would be 4 tiles or fewer.
- * rows = 64 or 128 forces that shape for every later plan and decode call in
- * the process (results agree within rounding; the softmax weights are
- * normalised per row either way).  Not synchronised with calls in flight on
- * other threads.  Returns MLA_ERR_BAD_SHAPE for any other value.
- */
-mla_status_t mla_set_group_rows(int32_t rows);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,6 @@
 // with the same log-sum-exp rule as the DCP exchange ("RFC: MsModeling 支持
 // Decode Context Parallel 仿真", §1.1, §2.1.4.3).
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -27,9 +26,6 @@ constexpr int kDefaultCus = 256;  // MI355X
 constexpr int kMaxShards = 4096;
 constexpr int kMaxTopK = 65536;
 constexpr int kMaxMergeParts = 1024;
-
-// Rows per work-group forced by mla_set_group_rows (0: chosen per problem).
-std::atomic<int> g_group_rows{0};
 
 struct Plan {
   int q_per_group, rows_per_group, q_groups, head_chunks, shard_units;
@@ -62,6 +58,7 @@ mla_status_t check_problem(const mla_problem_t *p) {
   if ((int64_t)p->max_seq_len > (int64_t)p->max_blocks * p->block_size) return MLA_ERR_BAD_SHAPE;
   if (p->max_seq_len < p->Q) return MLA_ERR_BAD_SHAPE;
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return MLA_ERR_BAD_SHAPE;
+  if (p->group_rows != 0 && p->group_rows != 64 && p->group_rows != 128) return MLA_ERR_BAD_SHAPE;
   if ((reinterpret_cast<uintptr_t>(p->q) | reinterpret_cast<uintptr_t>(p->kv)) & 15)
     return MLA_ERR_BAD_SHAPE;  // rows are moved in 16-byte pieces
   return MLA_OK;
@@ -132,7 +129,7 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   Plan wide, narrow;
   if (!layout(128, &wide) || !layout(64, &narrow)) return MLA_ERR_BAD_SHAPE;
   const int64_t wide_tiles = wide.chunk / kTile;
-  const int forced = g_group_rows.load(std::memory_order_relaxed);
+  const int forced = p->group_rows;
   const bool use_narrow =
       forced ? forced == 64
              : wide.rows_per_group <= 64 || (narrow.splits == 1 && wide.splits > 1) || wide_tiles <= 4;
@@ -319,12 +316,6 @@ const char *mla_status_string(mla_status_t s) {
     case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable gfx950 device";
   }
   return "unknown mla_status_t";
-}
-
-mla_status_t mla_set_group_rows(int32_t rows) {
-  if (rows != 0 && rows != 64 && rows != 128) return MLA_ERR_BAD_SHAPE;
-  g_group_rows.store(rows, std::memory_order_relaxed);
-  return MLA_OK;
 }
 
 mla_status_t mla_plan_query(const mla_problem_t *problem, int32_t num_shards, int32_t interleave,

@@ -39,7 +39,7 @@ class Problem(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("block_table", ctypes.c_void_p),
                 ("max_blocks", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
-                ("max_seq_len", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32), ("group_rows", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -71,8 +71,6 @@ def _load() -> ctypes.CDLL:
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_plan_query.argtypes = [P, i32, i32, i32, i32, i64, i32, ctypes.POINTER(Plan)]
     lib.mla_plan_query.restype = ctypes.c_int
-    lib.mla_set_group_rows.argtypes = [i32]
-    lib.mla_set_group_rows.restype = ctypes.c_int
     return lib
 
 
@@ -106,6 +104,12 @@ def _dtype_code(dtype) -> int:
     raise TypeError("output dtype must be bfloat16 or float32")
 
 
+# Work-group shape written into every problem this module builds (0: chosen
+# per problem, or 64 / 128 query rows per work-group); tests set it to run
+# each case under both shapes.
+GROUP_ROWS = 0
+
+
 def make_problem(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                  scale: float, max_seq_len: int) -> Problem:
     """mla_problem_t for q [B,Q,h_q,576] bf16, kv [N,bs,576] bf16, block_table [B,M] int32, seq_lens [B] int32."""
@@ -118,7 +122,7 @@ def make_problem(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, s
     B, Q, h_q, d_qk = q.shape
     return Problem(B, Q, h_q, d_qk, 512, float(scale), q.data_ptr(), kv.data_ptr(), kv.shape[0],
                    kv.shape[1], block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(),
-                   int(max_seq_len))
+                   int(max_seq_len), int(GROUP_ROWS))
 
 
 def mla_workspace_size(problem: Problem, num_shards: int = 1, shard_id: int = -1, top_k: int = 0) -> int:
@@ -134,11 +138,6 @@ def mla_plan_query(problem: Problem, num_shards: int = 1, interleave: int = 1, s
     _check(lib.mla_plan_query(ctypes.byref(problem), num_shards, interleave, shard_id, top_k,
                               index_stride_q, num_cus, ctypes.byref(plan)))
     return plan.as_dict()
-
-
-def mla_set_group_rows(rows: int) -> None:
-    """Force 64- or 128-row decode work-groups (0: chosen per problem)."""
-    _check(lib.mla_set_group_rows(rows))
 
 
 def _workspace(problem, num_shards, shard_id, top_k, workspace, device):

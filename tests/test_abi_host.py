@@ -59,7 +59,7 @@ def dense_status(p, num_shards=1, interleave=1, shard_id=-1, out=FAKE, dtype=0, 
     (dict(d_qk=512), 3), (dict(d_v=576), 3), (dict(h_q=129), 3), (dict(Q=17), 3),
     (dict(B=0), 2), (dict(h_q=0), 2), (dict(block_size=48), 2), (dict(block_size=0), 2),
     (dict(max_seq_len=2049 + 31 * 64), 2), (dict(max_seq_len=0), 2), (dict(scale=float("nan")), 2),
-    (dict(scale=0.0), 2), (dict(scale=-0.07), 2),
+    (dict(scale=0.0), 2), (dict(scale=-0.07), 2), (dict(group_rows=96), 2), (dict(group_rows=-64), 2),
     (dict(q=FAKE + 8), 2),
 ])
 def test_dense_validation_statuses(kw, status):
@@ -153,18 +153,16 @@ def test_plan_rejects_sparse_shards():
 
 
 def test_forced_group_rows_override_the_plan_and_reject_other_values():
-    dense = problem(B=32, max_seq_len=4096, max_blocks=64)
-    sparse = problem(B=32, max_seq_len=32768, max_blocks=512)
-    try:
-        md.mla_set_group_rows(64)
-        pl = plan(dense)
-        assert (pl["rows_per_group"], pl["units"], pl["splits"], pl["chunk"]) == (64, 64, 4, 1024)
-        md.mla_set_group_rows(128)
-        pl = plan(sparse, top_k=2048)
-        assert (pl["rows_per_group"], pl["units"], pl["splits"], pl["chunk"]) == (128, 32, 8, 256)
-        for bad in (-1, 1, 32, 96, 256):
-            assert lib.mla_set_group_rows(bad) == 2
-        assert plan(sparse, top_k=2048)["rows_per_group"] == 128  # a rejected value changes nothing
-    finally:
-        md.mla_set_group_rows(0)
-    assert plan(dense)["rows_per_group"] == 128 and plan(sparse, top_k=2048)["rows_per_group"] == 64
+    dense = dict(B=32, max_seq_len=4096, max_blocks=64)
+    sparse = dict(B=32, max_seq_len=32768, max_blocks=512)
+    pl = plan(problem(group_rows=64, **dense))
+    assert (pl["rows_per_group"], pl["units"], pl["splits"], pl["chunk"]) == (64, 64, 4, 1024)
+    pl = plan(problem(group_rows=128, **sparse), top_k=2048)
+    assert (pl["rows_per_group"], pl["units"], pl["splits"], pl["chunk"]) == (128, 32, 8, 256)
+    for bad in (-1, 1, 32, 96, 256):
+        st = lib.mla_plan_query(ctypes.byref(problem(group_rows=bad, **sparse)), 1, 1, -1, 2048, 0, 256,
+                                ctypes.byref(md.Plan()))
+        assert st == 2, bad
+    # the default picks per problem
+    assert plan(problem(**dense))["rows_per_group"] == 128
+    assert plan(problem(**sparse), top_k=2048)["rows_per_group"] == 64

@@ -32,9 +32,9 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True, params=[64, 128], ids=["rows64", "rows128"])
 def group_rows(request):
     """Every case runs with 64-row and with 128-row decode work-groups."""
-    md.mla_set_group_rows(request.param)
+    md.GROUP_ROWS = request.param
     yield request.param
-    md.mla_set_group_rows(0)
+    md.GROUP_ROWS = 0
 
 
 def ulp_bf16(x):
