@@ -137,6 +137,65 @@ def cpu_baseline(w, target_s: float, seed: int = 0):
                         f"{passes} full passes), fp64, {spent:.1f} s"))
 
 
+def run_kv_write(args, torch, md, W, dev):
+    """Latent KV-cache write: T = 32768 tokens per call into a 262144-slot cache
+    (302 MB), cycling through 8 input sets (302 MB of new rows) so the Infinity
+    Cache cannot serve them.  Bytes = each stored row read and written once
+    (2 x 1152 B) + the 4-byte slot of every token."""
+    T, num_slots, sets = 32768, 262144, 8
+    xs = [W.make_kv_write_inputs(T, num_slots, seed=2000 + r) for r in range(sets)]
+    rows = [torch.from_numpy(x.rows.view(np.int16)).to(dev).view(torch.bfloat16) for x in xs]
+    slots = [torch.from_numpy(x.slots).to(dev) for x in xs]
+    kv = torch.zeros((num_slots, 576), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        r = i % sets
+        md.mla_kv_write(rows[r], slots[r], kv, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    stored = float(np.mean([((x.slots >= 0) & (x.slots < num_slots)).sum() for x in xs]))
+    nbytes = stored * 2 * 1152 + T * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "latent KV-cache write (slot_mapping scatter) rows stored/s at 1 GPU; % of HBM roofline",
+        "value": stored / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"kv_write_t{T}_slots{num_slots}", "T": T, "num_slots": num_slots,
+                   "stored_rows_mean": stored, "rotating_input_sets": sets},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kv_write_kernel",
+                     "launch_ms": ms, "algorithmic_bytes": nbytes},
+    }
+    print(f"[bench] kv_write {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s algorithmic = {gbs / HBM_PEAK_GBS:.3f} "
+          f"of HBM peak", file=sys.stderr, flush=True)
+    rec["cpu_baseline"] = None
+    if args.cpu_seconds > 0:
+        from oracle import cache_ops
+        kv_host = np.zeros((num_slots, 576), dtype=np.uint16)
+        t0, done, n = time.perf_counter(), 0, 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            x = xs[n % sets]
+            kv_host = cache_ops.kv_write(kv_host, x.rows, x.slots)
+            done += int(((x.slots >= 0) & (x.slots < num_slots)).sum())
+            n += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} full calls ({done} rows stored) of the same workload, "
+                                         f"numpy, {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +205,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="distinct input sets cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--op", default="decode", choices=["decode", "kv_write"],
+                    help="decode: the attention call (default); kv_write: the latent-cache write "
+                         "through slot_mapping (32768 prefill tokens into a 262144-slot cache)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (the known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -170,6 +232,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+        return
+    if args.op == "kv_write":
+        run_kv_write(args, torch, md, W, dev)
         return
     t0 = time.time()
     w = W.CONFIGS[args.config]()

@@ -163,6 +163,39 @@ mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t
                            int64_t rows, int32_t d_v, void *out, mla_dtype_t out_dtype,
                            float *lse_out, void *stream);
 
+/*
+ * Latent KV-cache write: the step before attention that stores the new tokens'
+ * latent rows into the paged cache through a slot map ("RFC: MsModeling 支持
+ * Decode Context Parallel 仿真", §2.1.4.1, table A: the MLA cache
+ * [N_blk, block_size, kv_lora_rank + qk_rope_head_dim] and the int32
+ * slot_mapping [total_num_tokens]; under DCP the physical cache and the slot
+ * map keep their shapes and tokens are routed to ranks by interleaving at
+ * cp_kv_cache_interleave_size).  For every token t:
+ *
+ *   if slot_mapping[t] in [0, num_slots) and (num_shards == 1 or
+ *      floor(positions[t] / interleave) mod num_shards == shard_id):
+ *     kv[slot_mapping[t], 0:576] = rows[t, 0:576]      (a bitwise copy)
+ *
+ * A negative slot marks a token this call does not store (padding, or a token
+ * another rank owns); slots at or past num_slots are skipped, never written.
+ * Slots stored by one call must be distinct (with a repeated slot, which of
+ * the rows lands there is unspecified).  The copy moves each 1152-byte row with
+ * 16-byte vector loads and stores.
+ *
+ *  rows          device, bf16 [T, 576], 16-byte aligned
+ *  slot_mapping  device, int32 [T]
+ *  T             >= 0 (0 enqueues nothing)
+ *  kv            device, bf16 [num_slots, 576] (= [num_blocks, block_size, 576]),
+ *                16-byte aligned; updated in place
+ *  num_slots     num_blocks * block_size, >= 1
+ *  positions     device, int32 [T] token positions; read only when num_shards > 1
+ *  num_shards    >= 1; interleave >= 1; shard_id in [0, num_shards)
+ *                (ignored when num_shards == 1)
+ */
+mla_status_t mla_kv_write(const void *rows, const int32_t *slot_mapping, int64_t T, void *kv,
+                          int64_t num_slots, const int32_t *positions, int32_t num_shards,
+                          int32_t interleave, int32_t shard_id, void *stream);
+
 /* Static, human-readable name of a status. */
 const char *mla_status_string(mla_status_t status);
 

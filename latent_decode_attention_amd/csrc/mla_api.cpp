@@ -305,6 +305,29 @@ mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t
   return MLA_OK;
 }
 
+mla_status_t mla_kv_write(const void *rows, const int32_t *slot_mapping, int64_t T, void *kv,
+                          int64_t num_slots, const int32_t *positions, int32_t num_shards,
+                          int32_t interleave, int32_t shard_id, void *stream) {
+  if (T < 0 || num_slots < 1 || num_slots > INT32_MAX) return MLA_ERR_BAD_SHAPE;
+  if (num_shards < 1 || num_shards > kMaxShards) return MLA_ERR_BAD_SHAPE;
+  if (num_shards > 1 && (interleave < 1 || shard_id < 0 || shard_id >= num_shards)) return MLA_ERR_BAD_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!rows || !slot_mapping || !kv || (num_shards > 1 && !positions)) return MLA_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(kv)) & 15) return MLA_ERR_BAD_SHAPE;
+  KvWriteArgs a;
+  a.rows = rows;
+  a.slots = slot_mapping;
+  a.T = T;
+  a.kv = kv;
+  a.num_slots = num_slots;
+  a.positions = positions;
+  a.num_shards = num_shards;
+  a.interleave = num_shards > 1 ? interleave : 1;
+  a.shard_id = num_shards > 1 ? shard_id : 0;
+  if (launch_kv_write(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
 const char *mla_status_string(mla_status_t s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

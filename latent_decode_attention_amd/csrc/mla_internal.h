@@ -62,8 +62,20 @@ struct MergeArgs {
   float *lse_out;         // [groups, rows]
 };
 
+// Latent KV-cache write through a slot map (optionally one DCP shard's tokens).
+struct KvWriteArgs {
+  const void *rows;            // bf16 [T, 576]
+  const int32_t *slots;        // [T]
+  int64_t T;
+  void *kv;                    // bf16 [num_slots, 576]
+  int64_t num_slots;
+  const int32_t *positions;    // [T], read only when num_shards > 1
+  int32_t num_shards, interleave, shard_id;
+};
+
 // Enqueue the kernels; return the HIP status of the launch.
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteArgs &args, hipStream_t stream);
 
 }  // namespace mla

@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -1051,6 +1052,50 @@ __global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeA
   if (lane == 0) a.lse_out[out_row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
+// Latent KV-cache write: each wave moves kKvRowsPerWave token rows per pass
+// (rows strided over the grid; one row per wave and as many waves as rows, up
+// to 32 per CU, measured fastest), loading before storing; lanes move a row's
+// 72 chunks of 16 bytes in two passes (64 + 8), so the reads and writes are
+// whole 128-byte lines.  Tokens with a negative or out-of-range slot, or (DCP) owned by
+// another shard, are skipped.
+constexpr int kKvWriteThreads = 256;
+constexpr int kKvRowsPerWave = 1;
+__global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWriteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (kKvWriteThreads / 64);
+  const int64_t wave0 = (int64_t)blockIdx.x * (kKvWriteThreads / 64) + (threadIdx.x >> 6);
+  for (int64_t t0 = wave0; t0 < a.T; t0 += waves * kKvRowsPerWave) {
+    u32x4 v[kKvRowsPerWave][2];
+    int64_t dst_row[kKvRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kKvRowsPerWave; ++k) {
+      const int64_t t = t0 + k * waves;
+      dst_row[k] = -1;
+      if (t < a.T) {
+        const int slot = a.slots[t];
+        bool store = slot >= 0 && slot < a.num_slots;
+        if (a.num_shards > 1) {
+          const int p = a.positions[t];
+          store = store && p >= 0 && (p / a.interleave) % a.num_shards == a.shard_id;
+        }
+        if (store) {
+          const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.rows) + t * kRowBytes);
+          v[k][0] = src[lane];
+          if (lane < kChunks - 64) v[k][1] = src[64 + lane];
+          dst_row[k] = slot;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kKvRowsPerWave; ++k) {
+      if (dst_row[k] < 0) continue;  // the whole wave takes the same branch
+      u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.kv) + dst_row[k] * kRowBytes);
+      dst[lane] = v[k][0];
+      if (lane < kChunks - 64) dst[64 + lane] = v[k][1];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
@@ -1066,6 +1111,14 @@ hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t strea
     if (wide) hipLaunchKernelGGL((decode_kernel<kDenseStream, 128>), g, b, 0, stream, args);
     else hipLaunchKernelGGL((decode_kernel<kDenseStream, 64>), g, b, 0, stream, args);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const KvWriteArgs &args, hipStream_t stream) {
+  // Enough waves to keep every CU's memory pipeline busy; each strides over rows.
+  const int64_t rows_per_block = kKvWriteThreads / 64 * kKvRowsPerWave;
+  const int64_t blocks = std::min<int64_t>((args.T + rows_per_block - 1) / rows_per_block, 256 * 32);
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(kKvWriteThreads), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_sparse.restype = ctypes.c_int
     lib.mla_merge_lse.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp, vp]
     lib.mla_merge_lse.restype = ctypes.c_int
+    lib.mla_kv_write.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, vp]
+    lib.mla_kv_write.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_plan_query.argtypes = [P, i32, i32, i32, i32, i64, i32, ctypes.POINTER(Plan)]
@@ -221,3 +223,26 @@ def mla_merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out: Option
     _check(lib.mla_merge_lse(_ptr(o_parts), _ptr(lse_parts), n, rows, d_v, _ptr(out),
                              _dtype_code(out.dtype), _ptr(lse_out), _stream(stream)))
     return out, lse_out
+
+
+def mla_kv_write(rows: torch.Tensor, slot_mapping: torch.Tensor, kv: torch.Tensor, *,
+                 positions: Optional[torch.Tensor] = None, num_shards: int = 1, interleave: int = 1,
+                 shard_id: int = 0, stream=None) -> torch.Tensor:
+    """Store rows [T, 576] bf16 into the paged cache kv [num_blocks, block_size, 576] bf16
+    at slot_mapping [T] int32 (negative: not stored); with num_shards > 1 only the
+    tokens whose positions [T] int32 this shard owns.  Updates kv in place."""
+    if rows.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise TypeError("rows and kv must be bfloat16")
+    if slot_mapping.dtype != torch.int32 or (positions is not None and positions.dtype != torch.int32):
+        raise TypeError("slot_mapping and positions must be int32")
+    for name, t in (("rows", rows), ("slot_mapping", slot_mapping), ("kv", kv), ("positions", positions)):
+        if t is not None and (not t.is_contiguous() or not t.is_cuda):
+            raise TypeError(f"{name} must be a contiguous GPU tensor")
+    T = rows.shape[0] if rows.dim() == 2 else 0
+    if rows.dim() != 2 or rows.shape[1] != 576 or slot_mapping.numel() != T or kv.shape[-1] != 576:
+        raise TypeError("expected rows [T, 576], slot_mapping [T], kv [..., 576]")
+    if positions is not None and positions.numel() != T:
+        raise TypeError("positions must have one entry per row")
+    _check(lib.mla_kv_write(_ptr(rows), _ptr(slot_mapping), T, _ptr(kv), kv.numel() // 576, _ptr(positions),
+                            num_shards, interleave, shard_id, _stream(stream)))
+    return kv

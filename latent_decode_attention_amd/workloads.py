@@ -280,3 +280,31 @@ def attended_count(w: Workload) -> int:
                                             b * w.index_stride_b + qi * w.index_stride_q + w.top_k]
                 total += int(np.count_nonzero((lst >= 0) & (lst <= last)))
     return total
+
+
+@dataclass
+class KvWriteInputs:
+    """Seeded inputs of one latent-cache write: T new rows, their slots and positions."""
+    rows: np.ndarray       # uint16 [T, 576] bf16 bits
+    slots: np.ndarray      # int32 [T]: distinct slots, some -1 (not stored) and some >= num_slots
+    positions: np.ndarray  # int32 [T]
+    num_slots: int
+
+
+def make_kv_write_inputs(T: int, num_slots: int, seed: int, skip_frac: float = 0.1,
+                         out_of_range: int = 2) -> KvWriteInputs:
+    """T rows of N(0,1) -> bf16 bits; distinct slots drawn from [0, num_slots) (a
+    skip_frac share replaced by -1, and `out_of_range` entries set at or past the
+    end of the cache); positions 0..T-1 shuffled (a prefill's tokens)."""
+    g_rows, g_slots, g_pos = _children(seed, 3)
+    rows = _normal_bf16(g_rows, (T, D_QK))
+    slots = g_slots.choice(num_slots, size=T, replace=False).astype(np.int32) if T <= num_slots else \
+        np.arange(T, dtype=np.int32) % num_slots
+    if T:
+        skip = g_slots.random(T) < skip_frac
+        slots[skip] = -1
+        k = min(out_of_range, T)
+        far = g_slots.choice(T, size=k, replace=False)
+        slots[far] = num_slots + np.arange(k, dtype=np.int32)
+    positions = g_pos.permutation(T).astype(np.int32)
+    return KvWriteInputs(rows=rows, slots=slots, positions=positions, num_slots=num_slots)

@@ -166,3 +166,18 @@ def test_forced_group_rows_override_the_plan_and_reject_other_values():
     # the default picks per problem
     assert plan(problem(**dense))["rows_per_group"] == 128
     assert plan(problem(**sparse), top_k=2048)["rows_per_group"] == 64
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(T=-1), 2), (dict(num_slots=0), 2), (dict(num_slots=1 << 31), 2),
+    (dict(num_shards=0), 2), (dict(num_shards=2, interleave=0), 2), (dict(num_shards=2, shard_id=2), 2),
+    (dict(num_shards=2, shard_id=-1), 2), (dict(rows=None), 1), (dict(slots=None), 1), (dict(kv=None), 1),
+    (dict(num_shards=2, positions=None), 1), (dict(rows=FAKE + 8), 2), (dict(kv=FAKE + 4), 2),
+    (dict(T=0, rows=None, slots=None, kv=None), 0),
+])
+def test_kv_write_argument_checks(args, status):
+    a = dict(rows=FAKE, slots=FAKE, T=10, kv=FAKE, num_slots=100, positions=FAKE, num_shards=1,
+             interleave=1, shard_id=0)
+    a.update(args)
+    assert lib.mla_kv_write(a["rows"], a["slots"], a["T"], a["kv"], a["num_slots"], a["positions"],
+                            a["num_shards"], a["interleave"], a["shard_id"], None) == status
