@@ -49,6 +49,7 @@ def _load():
     lib.oracle_dense.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                  i64p, dp, dp]
     lib.oracle_sparse.argtypes = [P, i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int64, i64p, dp, dp]
     lib.oracle_merge.argtypes = [dp, dp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, dp, dp]
     for f in (lib.oracle_dense, lib.oracle_sparse, lib.oracle_merge):
@@ -113,8 +114,10 @@ def dense(w, rows=None, num_shards: int = 1, interleave: int = 1, shard_id: int 
     return out, lse
 
 
-def sparse(w, rows=None, indices=None, top_k=None, stride_b=None, stride_q=None):
-    """Sparse (top-k) decode for the selected output rows."""
+def sparse(w, rows=None, indices=None, top_k=None, stride_b=None, stride_q=None,
+           num_shards: int = 1, interleave: int = 1, shard_id: int = 0):
+    """Sparse (top-k) decode for the selected output rows (optionally one DCP shard:
+    only the listed positions that shard holds)."""
     lib = _load()
     keep: list = []
     p = _problem(w, keep)
@@ -127,7 +130,8 @@ def sparse(w, rows=None, indices=None, top_k=None, stride_b=None, stride_q=None)
     sel, n = _sel(w, rows)
     out = np.zeros((n, w.d_v), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
-    rc = lib.oracle_sparse(ctypes.byref(p), _ptr(idx, ctypes.c_int32), top_k, stride_b, stride_q, n,
+    rc = lib.oracle_sparse(ctypes.byref(p), _ptr(idx, ctypes.c_int32), top_k, stride_b, stride_q,
+                           num_shards, interleave, shard_id, n,
                            None if sel is None else _ptr(sel, ctypes.c_int64),
                            _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
     _check(rc)

@@ -185,14 +185,21 @@ int oracle_dense(const oracle_problem *P, int32_t num_shards, int32_t interleave
 /*
  * Sparse (SFA) decode.  indices[b * stride_b + q * stride_q + k], k < top_k,
  * are logical positions; the attended multiset for (b, q) holds each entry i
- * with 0 <= i <= S_b - Q + q (so -1 padding and out-of-range values drop out).
+ * with 0 <= i <= S_b - Q + q (so -1 padding and out-of-range values drop out),
+ * and with num_shards > 1 only the entries this DCP rank holds,
+ * floor(i / interleave) mod num_shards == shard_id (the interleaved placement
+ * of the DCP page, §2.1.4.1; sparse attention under DCP attends, on each rank,
+ * the selected positions that rank stores).
  */
 int oracle_sparse(const oracle_problem *P, const int32_t *indices, int32_t top_k,
-                  int64_t stride_b, int64_t stride_q, int64_t n_sel, const int64_t *sel,
-                  double *out, double *lse) {
+                  int64_t stride_b, int64_t stride_q, int32_t num_shards, int32_t interleave,
+                  int32_t shard_id, int64_t n_sel, const int64_t *sel, double *out, double *lse) {
   int rc = check_problem(P);
   if (rc) return rc;
   if (!indices || top_k < 0 || !out || !lse) return ORACLE_ERR_ARG;
+  if (num_shards < 1 || (num_shards > 1 && (interleave < 1 || shard_id < 0 ||
+                                            shard_id >= num_shards)))
+    return ORACLE_ERR_ARG;
   int64_t rows = (int64_t)P->B * P->Q * P->h_q;
   if (!sel) n_sel = rows;
   int err = ORACLE_OK;
@@ -220,7 +227,8 @@ int oracle_sparse(const oracle_problem *P, const int32_t *indices, int32_t top_k
     int64_t n = 0;
     for (int32_t k = 0; k < top_k; ++k) {
       int64_t i = list[k];
-      if (i >= 0 && i <= last) pos[n++] = i;
+      if (i >= 0 && i <= last && (num_shards == 1 || (i / interleave) % num_shards == shard_id))
+        pos[n++] = i;
     }
     int e = attend(P, b, qi, h, pos, n, s, out + t * P->d_v, lse + t);
     if (e) {

@@ -185,6 +185,48 @@ def test_one_hot_probe_sparse_multiplicity_and_padding():
     np.testing.assert_allclose(out[0], expect, atol=1e-15)
 
 
+@pytest.mark.parametrize("N,I", [(2, 1), (3, 4), (8, 2)])
+def test_one_hot_probe_sparse_shards_keep_the_entries_each_shard_holds(N, I):
+    S = 30
+    rows = _one_hot_rows(S)
+    q = np.zeros((1, 1, 1, D_QK), dtype=np.uint16)
+    idx = np.array([4, 4, -1, 29, 31, 0, -1, 17, 9, 22, 13, 5], dtype=np.int32)
+    w = workload(q, [rows], block_size=4, seed=15, indices=idx, top_k=12, index_stride_b=12,
+                 index_stride_q=0)
+    for r in range(N):
+        out, lse = oracle.sparse(w, num_shards=N, interleave=I, shard_id=r)
+        mine = [int(i) for i in idx if 0 <= i < S and (i // I) % N == r]
+        if not mine:
+            assert lse[0] == -np.inf and np.all(out[0] == 0)
+            continue
+        assert abs(lse[0] - math.log(len(mine))) < 1e-14
+        expect = np.zeros(D_V)
+        for i in mine:
+            expect[i] += 1 / len(mine)
+        np.testing.assert_allclose(out[0], expect, atol=1e-15)
+
+
+@pytest.mark.parametrize("N,I", [(2, 1), (3, 4), (8, 16)])
+def test_sparse_shards_then_merge_equal_unsharded(N, I):
+    rng = np.random.default_rng(40 + N)
+    S = [300, 129, 77]
+    Q, H, K = 2, 2, 64
+    logical = [random_rows(rng, s) for s in S]
+    q = random_rows(rng, len(S) * Q * H).reshape(len(S), Q, H, D_QK)
+    idx = np.full((len(S), Q, K), -1, dtype=np.int32)
+    for b, s in enumerate(S):
+        for qi in range(Q):
+            n = min(K - 3, s)
+            idx[b, qi, :n] = rng.choice(s, size=n, replace=False)
+    w = workload(q, logical, block_size=16, seed=41, indices=idx.reshape(-1), top_k=K,
+                 index_stride_b=Q * K, index_stride_q=K)
+    full_o, full_l = oracle.sparse(w)
+    parts = [oracle.sparse(w, num_shards=N, interleave=I, shard_id=r) for r in range(N)]
+    mo, ml = oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(ml, full_l, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mo, full_o, rtol=0, atol=1e-12)
+
+
 def test_empty_attended_set_gives_zero_and_minus_inf():
     rng = np.random.default_rng(16)
     rows = random_rows(rng, 10)
