@@ -20,7 +20,9 @@ MUTATIONS = {
     "dot_over_v_columns_only": ("for (int k = 0; k < D; ++k) dot", "for (int k = 0; k < DV; ++k) dot"),
     "v_from_wrong_columns": ("out[c] += w * bf16_value(vrow[c]);", "out[c] += w * bf16_value(vrow[c + 64]);"),
     "causal_off_by_one": ("for (int64_t p = 0; p <= last; ++p)", "for (int64_t p = 0; p < last; ++p)"),
-    "sparse_no_causal_filter": ("if (i >= 0 && i <= last) pos[n++] = i;", "if (i >= 0 && i < P->seq_lens[b]) pos[n++] = i;"),
+    "sparse_no_causal_filter": ("if (i >= 0 && i <= last && (", "if (i >= 0 && i < P->seq_lens[b] && ("),
+    "sparse_shard_rule_by_token": ("(i / interleave) % num_shards == shard_id", "i % num_shards == shard_id"),
+    "sparse_shard_filter_dropped": ("(num_shards == 1 || (i / interleave)", "(1 || (i / interleave)"),
     "identity_block_mapping": ("return (int64_t)blk * P->block_size + p % P->block_size;",
                                "return (int64_t)b * P->max_blocks * P->block_size + p;"),
     "shard_rule_by_token": ("(p / interleave) % num_shards == shard_id", "p % num_shards == shard_id"),
