@@ -146,6 +146,29 @@ mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indi
                                size_t workspace_bytes, void *stream);
 
 /*
+ * Sparse decode under decode context parallelism: the index list of each
+ * (b, q) is the globally selected top-k, and DCP rank r attends the listed
+ * positions it holds, floor(i / interleave) mod num_shards == r (the
+ * interleaved placement of "RFC: MsModeling 支持 Decode Context Parallel 仿真",
+ * §2.1.4.1; sparse attention combined with DCP is that page's follow-up work,
+ * §3.3).  Each shard emits its fp32 (O, lse) partial, which mla_merge_lse
+ * combines exactly as for dense DCP; a shard that holds none of a row's
+ * positions gives O = 0, lse = -inf for that row.
+ *
+ *  problem, indices, top_k, index_stride_b, index_stride_q  as mla_decode_sparse.
+ *  num_shards  2..4096;  interleave >= 1;  shard_id in [0, num_shards) for one
+ *              shard, or -1 for all shards in one call.
+ *  out         device, fp32 [n_out, B, Q, h_q, 512], n_out = num_shards if
+ *              shard_id = -1, else 1;  lse  device, fp32 [n_out, B, Q, h_q].
+ *  workspace   >= mla_workspace_size(problem, num_shards, shard_id, top_k) bytes.
+ */
+mla_status_t mla_decode_sparse_dcp(const mla_problem_t *problem, const int32_t *indices,
+                                   int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
+                                   int32_t num_shards, int32_t interleave, int32_t shard_id,
+                                   float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/*
  * Online-softmax merge of n partial results ("RFC: MsModeling 支持 Decode
  * Context Parallel 仿真", §1.1 and §2.1.4.3: after the exchange the partial
  * outputs and lse are recombined locally).  For every row r:

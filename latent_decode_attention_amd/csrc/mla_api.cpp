@@ -69,10 +69,8 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   const bool sparse = top_k > 0;
   if (top_k < 0 || top_k > kMaxTopK) return MLA_ERR_BAD_SHAPE;
   if (num_shards < 1 || num_shards > kMaxShards) return MLA_ERR_BAD_SHAPE;
-  if (num_shards > 1) {
-    if (sparse) return MLA_ERR_UNSUPPORTED;
-    if (interleave < 1 || shard_id < -1 || shard_id >= num_shards) return MLA_ERR_BAD_SHAPE;
-  }
+  if (num_shards > 1 && (interleave < 1 || shard_id < -1 || shard_id >= num_shards))
+    return MLA_ERR_BAD_SHAPE;
   if (num_cus < 1) num_cus = kDefaultCus;
   int64_t L;
   if (sparse) {
@@ -276,6 +274,23 @@ mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indi
   if (st != MLA_OK) return st;
   return run(problem, pl, true, indices, top_k, index_stride_b, index_stride_q, 1, 1, -1, out,
              out_dtype == MLA_DTYPE_FP32, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_decode_sparse_dcp(const mla_problem_t *problem, const int32_t *indices,
+                                   int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
+                                   int32_t num_shards, int32_t interleave, int32_t shard_id,
+                                   float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  mla_status_t st = check_problem(problem);
+  if (st != MLA_OK) return st;
+  if (!indices || !out || !lse) return MLA_ERR_NULL_POINTER;
+  if (top_k < 1 || index_stride_b < 0 || index_stride_q < 0) return MLA_ERR_BAD_SHAPE;
+  if (num_shards < 2) return MLA_ERR_BAD_SHAPE;
+  Plan pl;
+  st = make_plan(problem, num_shards, interleave, shard_id, top_k, index_stride_q, device_cus(), &pl);
+  if (st != MLA_OK) return st;
+  return run(problem, pl, true, indices, top_k, index_stride_b, index_stride_q, num_shards, interleave,
+             shard_id, out, true, lse, workspace, workspace_bytes, stream);
 }
 
 mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t n,

@@ -222,11 +222,19 @@ __device__ __forceinline__ int raw_block(const DecodeArgs &a, const Unit &u, int
   const int slot = min(max(p, 0) >> a.bs_shift, a.max_blocks - 1);
   return u.bt[slot];
 }
-// Physical cache row of a token, or -1 when no query row of this group attends it.
+// Physical cache row of a token, or -1 when no query row of this group attends
+// it.  A sparse list under DCP keeps only the positions this shard holds,
+// floor(p / interleave) mod N = shard (the DCP page's interleaved placement,
+// §2.1.4.1); dense shard streams only ever produce such positions.
+template <int kMode>
 __device__ __forceinline__ int token_row(const DecodeArgs &a, const Unit &u, int i, int p, int blk) {
   const int last = u.S - a.Q + u.q0 + a.q_per_group - 1;
-  const bool ok = i < u.i1 && p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && blk >= 0 &&
-                  blk < a.num_blocks;
+  bool ok = i < u.i1 && p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && blk >= 0 &&
+            blk < a.num_blocks;
+  if constexpr (kMode == kSparseStream) {
+    if (a.num_shards > 1)
+      ok = ok && ((unsigned)p / (unsigned)a.interleave) % (unsigned)a.num_shards == (unsigned)u.shard;
+  }
   return ok ? blk * a.block_size + (p & (a.block_size - 1)) : -1;
 }
 
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     __builtin_amdgcn_sched_barrier(0);
     after_blocks();
     __builtin_amdgcn_sched_barrier(0);
-    const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
+    const int row0 = token_row<kMode>(a, u, u.i0 + plane, p0, b0);
     copy_all(prepare_copy(sm.tile[0], a, wave, lane, row0));
     mask_cur = tile_mask(a, u, p0, row0);
   };
@@ -581,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       TileCopy next_copy;
       auto tile_step_work = [&](int step) {
         if (step == 0) {
-          row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
+          row1 = token_row<kMode>(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
           crow = copy_rows(row1, wave, lane);
         }
         if (step == 2) next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);

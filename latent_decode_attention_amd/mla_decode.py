@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_merge_lse.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp, vp]
     lib.mla_merge_lse.restype = ctypes.c_int
     lib.mla_kv_write.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, vp]
+    lib.mla_decode_sparse_dcp.argtypes = [P, vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.mla_decode_sparse_dcp.restype = ctypes.c_int
     lib.mla_kv_write.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -177,10 +179,13 @@ def mla_decode_dense(q, kv, block_table, seq_lens, *, scale: float, max_seq_len:
 
 def mla_decode_sparse(q, kv, block_table, seq_lens, indices, *, scale: float, max_seq_len: int,
                       top_k: Optional[int] = None, index_stride_b: Optional[int] = None,
-                      index_stride_q: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                      index_stride_q: Optional[int] = None, num_shards: int = 1, interleave: int = 1,
+                      shard_id: int = -1, out: Optional[torch.Tensor] = None,
                       lse: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                       workspace: Optional[torch.Tensor] = None, stream=None):
-    """Sparse top-k decode.  indices: int32, [B, top_k] (shared across Q) or [B, Q, top_k]."""
+    """Sparse top-k decode.  indices: int32, [B, top_k] (shared across Q) or [B, Q, top_k].
+    With num_shards > 1 (mla_decode_sparse_dcp) each DCP shard attends the listed
+    positions it holds and emits fp32 partials [n_out, B, Q, h_q, 512] and lse."""
     p = make_problem(q, kv, block_table, seq_lens, scale, max_seq_len)
     if indices.dtype != torch.int32 or not indices.is_contiguous() or not indices.is_cuda:
         raise TypeError("indices must be a contiguous int32 GPU tensor")
@@ -194,6 +199,21 @@ def mla_decode_sparse(q, kv, block_table, seq_lens, indices, *, scale: float, ma
     need = (B - 1) * index_stride_b + (Q - 1) * index_stride_q + top_k
     if indices.numel() < need:
         raise TypeError("indices is smaller than its strides imply")
+    if num_shards > 1:
+        n_out = num_shards if shard_id < 0 else 1
+        if out is None:
+            out = torch.empty((n_out, B, Q, h_q, 512), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((n_out, B, Q, h_q), dtype=torch.float32, device=q.device)
+        if (tuple(out.shape) != (n_out, B, Q, h_q, 512) or out.dtype != torch.float32 or
+                tuple(lse.shape) != (n_out, B, Q, h_q) or lse.dtype != torch.float32):
+            raise TypeError("sharded out/lse must be fp32 [n_out, B, Q, h_q, 512] and [n_out, B, Q, h_q]")
+        workspace = _workspace(p, num_shards, shard_id, top_k, workspace, q.device)
+        _check(lib.mla_decode_sparse_dcp(ctypes.byref(p), _ptr(indices), top_k, index_stride_b,
+                                         index_stride_q, num_shards, interleave, shard_id, _ptr(out),
+                                         _ptr(lse), _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(), _stream(stream)))
+        return out, lse
     if out is None:
         out = torch.empty((B, Q, h_q, 512), dtype=out_dtype, device=q.device)
     if lse is None:

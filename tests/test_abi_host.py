@@ -147,9 +147,28 @@ def test_plan_shards_cover_their_positions(S, N, I):
         assert pl["grid"] == units * pl["splits"]
 
 
-def test_plan_rejects_sparse_shards():
-    assert lib.mla_plan_query(ctypes.byref(problem()), 2, 64, -1, 2048, 0, 256,
-                              ctypes.byref(md.Plan())) == 3
+def test_plan_sparse_shards():
+    # sparse x DCP: every shard streams the whole list (the shard keeps its own entries)
+    pl = plan(problem(B=8, max_seq_len=131072, max_blocks=2048), top_k=2048, num_shards=8, interleave=64,
+              shard_id=-1)
+    assert pl["stream_len"] == 2048
+    assert pl["units"] == 8 * 8 * (128 // pl["rows_per_group"])  # sequences x shards x head chunks
+    assert pl["grid"] == pl["units"] * pl["splits"]
+    one = plan(problem(B=8, max_seq_len=131072, max_blocks=2048), top_k=2048, num_shards=8, interleave=64,
+               shard_id=3)
+    assert one["stream_len"] == 2048 and one["units"] == 8 * (128 // one["rows_per_group"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_shards=1), 2), (dict(num_shards=0), 2), (dict(shard_id=8), 2), (dict(shard_id=-2), 2),
+    (dict(interleave=0), 2), (dict(indices=None), 1), (dict(out=None), 1), (dict(top_k=0), 2),
+])
+def test_sparse_dcp_argument_checks(kw, status):
+    a = dict(indices=FAKE, top_k=64, num_shards=8, interleave=64, shard_id=-1, out=FAKE)
+    a.update(kw)
+    assert lib.mla_decode_sparse_dcp(ctypes.byref(problem()), a["indices"], a["top_k"], 64, 0,
+                                     a["num_shards"], a["interleave"], a["shard_id"], a["out"], FAKE,
+                                     None, 0, None) == status
 
 
 def test_forced_group_rows_override_the_plan_and_reject_other_values():

@@ -218,6 +218,58 @@ def test_one_hot_probe_sparse_padding_duplicates():
         assert abs(lse.cpu().numpy().reshape(Q, 32)[qi, 5] - math.log(len(valid))) < 1e-5
 
 
+@pytest.mark.parametrize("N,I", [(3, 16), (8, 2)])
+def test_one_hot_probe_sparse_dcp_shards(N, I):
+    # Each shard recovers exactly the listed positions it holds, with multiplicity.
+    S, Q = 400, 2
+    idx = np.full(300, -1, dtype=np.int32)
+    idx[:250] = np.random.default_rng(6).choice(S, 250, replace=False)
+    idx[250:256] = [S - 1, S - 1, 7, 100000, -3, 7]
+    w = one_hot_workload(S, Q, 16, seed=10, indices=idx, top_k=300, index_stride_b=300, index_stride_q=0)
+    d = upload(w)
+    out, lse = md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, d.indices, scale=w.scale,
+                                    max_seq_len=w.max_seq_len, top_k=300, index_stride_b=300, index_stride_q=0,
+                                    num_shards=N, interleave=I, shard_id=-1)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(N, Q, 32, 512)
+    l = lse.cpu().numpy().reshape(N, Q, 32)
+    for r in range(N):
+        for qi in range(Q):
+            last = S - Q + qi
+            mine = [int(i) for i in idx if 0 <= i <= last and (i // I) % N == r]
+            if not mine:
+                assert np.all(o[r, qi] == 0) and np.all(np.isneginf(l[r, qi]))
+                continue
+            counts = np.bincount(mine, minlength=512) / len(mine)
+            np.testing.assert_allclose(o[r, qi, 5], counts, rtol=1e-6, atol=0)
+            assert abs(l[r, qi, 5] - math.log(len(mine))) < 1e-5
+
+
+def test_sparse_dcp_shards_match_the_oracle_and_merge_to_unsharded():
+    N, I = 4, 16
+    w = W.make_workload("sparse_dcp", 4, 2, 64, [3000, 700, 2049, 129], 16, seed=71, top_k=512)
+    d = upload(w)
+    kw = dict(scale=w.scale, max_seq_len=w.max_seq_len, top_k=w.top_k, index_stride_b=w.index_stride_b,
+              index_stride_q=w.index_stride_q)
+    parts, plse = md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, d.indices, num_shards=N,
+                                       interleave=I, shard_id=-1, **kw)
+    torch.cuda.synchronize()
+    for r in range(N):
+        ro, rl = oracle.sparse(w, num_shards=N, interleave=I, shard_id=r)
+        assert_o_close(parts[r], ro, f"shard {r}")
+        assert_lse_close(plse[r], rl, f"shard {r}")
+    # one shard at a time gives the same bytes as the all-shards call
+    one, one_l = md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, d.indices, num_shards=N,
+                                      interleave=I, shard_id=2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], parts[2]) and torch.equal(one_l[0], plse[2])
+    merged, mlse = md.mla_merge_lse(parts.contiguous(), plse.contiguous(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse(w)
+    assert_o_close(merged, ro, "merged")
+    assert_lse_close(mlse, rl, "merged")
+
+
 def test_nan_poison_in_unreferenced_rows_never_reaches_output():
     w = W.make_workload("poison", 2, 2, 64, [900, 2000], 64, seed=61, top_k=333)
     ref = oracle.sparse(w)
