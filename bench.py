@@ -48,7 +48,7 @@ def algorithmic_work(w, indices_list=None):
 
     bytes = latent rows attended (each once per sequence) x 1152 + q + O + lse
             + index lists + block-table entries of the blocks touched
-            (+ the fp32 shard partials written and read, for sharded dense).
+            (+ the fp32 shard partials written and read, under DCP).
     flops = sum_{b,q} |A(b,q)| * h_q * 2 * (576 + 512).
     """
     B, Q, H = w.B, w.Q, w.h_q
@@ -201,7 +201,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, help="workload preset (1..6); 3 = sparse S=32k")
+    ap.add_argument("--config", type=int, default=3, help="workload preset (1..7); 3 = sparse S=32k")
     ap.add_argument("--rotate", type=int, default=8, help="distinct input sets cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
@@ -275,14 +275,15 @@ def main():
         if idx_dev is not None:
             md.mla_decode_sparse(d.q, d.kv, d.block_table, d.seq_lens, idx_dev[r], scale=w.scale,
                                  max_seq_len=w.max_seq_len, top_k=w.top_k, index_stride_b=w.index_stride_b,
-                                 index_stride_q=w.index_stride_q, out=out, lse=lse,
+                                 index_stride_q=w.index_stride_q, num_shards=w.num_shards,
+                                 interleave=w.interleave, shard_id=-1, out=out, lse=lse,
                                  workspace=workspace, stream=stream)
         else:
             md.mla_decode_dense(d.q, kv_dev[r], d.block_table, d.seq_lens, scale=w.scale,
                                 max_seq_len=w.max_seq_len, num_shards=w.num_shards, interleave=w.interleave,
                                 shard_id=-1, out=out, lse=lse, workspace=workspace, stream=stream)
-            if sharded:
-                md.mla_merge_lse(out, lse, out=merged, lse_out=mlse, stream=stream)
+        if sharded:
+            md.mla_merge_lse(out, lse, out=merged, lse_out=mlse, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -343,7 +344,8 @@ def main():
                      "frac": (achieved_gbs / HBM_PEAK_GBS) if bound == "hbm" else
                              (achieved_tfs / MFMA_BF16_PEAK_TFS),
                      "traffic": traffic,
-                     "kernel": "decode_kernel" + ("+merge_kernel" if splits > 1 or sharded else ""),
+                     "kernel": (("partition_kernel+" if sharded and w.indices is not None else "") +
+                                "decode_kernel" + ("+merge_kernel" if splits > 1 or sharded else "")),
                      "launch_ms": call_ms,
                      "mfma_tflops": achieved_tfs,
                      "mfma_frac": achieved_tfs / MFMA_BF16_PEAK_TFS,

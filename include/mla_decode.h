@@ -88,9 +88,10 @@ typedef struct {
 
 /*
  * Bytes of scratch the decode call needs for its split-KV partial results
- * (fp32 partial outputs plus their lse).  `top_k` = 0 sizes a dense call,
+ * (fp32 partial outputs plus their lse) and, for sparse calls under DCP, for
+ * each shard's part of the index lists.  `top_k` = 0 sizes a dense call,
  * > 0 a sparse call with that list length; `num_shards`/`shard_id` as in
- * mla_decode_dense.  Depends on the current HIP device's compute-unit count
+ * mla_decode_dense (num_shards > 1 with top_k > 0 sizes mla_decode_sparse_dcp).  Depends on the current HIP device's compute-unit count
  * (256 is assumed when no device is visible).  Returns 0 when the plan needs
  * no scratch, and (size_t)-1 when the arguments are invalid.
  */
@@ -110,7 +111,9 @@ size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards,
  *  num_shards  >= 1.  1 = unsharded; `interleave` and `shard_id` are ignored.
  *  interleave  >= 1 when num_shards > 1.
  *  shard_id    -1 = compute every shard in this call; otherwise one shard in
- *              [0, num_shards).
+ *              [0, num_shards).  The two forms agree within the stated accuracy,
+ *              not bit for bit: the plan (where partitions start, and so the
+ *              running maxima P is rounded against) depends on the work per call.
  *  out         device.  Unsharded: [B, Q, h_q, d_v] in out_dtype.  Sharded:
  *              fp32 [n_out, B, Q, h_q, d_v] with n_out = num_shards when
  *              shard_id = -1, else 1 (out_dtype must be MLA_DTYPE_FP32).
@@ -160,7 +163,13 @@ mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indi
  *              shard, or -1 for all shards in one call.
  *  out         device, fp32 [n_out, B, Q, h_q, 512], n_out = num_shards if
  *              shard_id = -1, else 1;  lse  device, fp32 [n_out, B, Q, h_q].
- *  workspace   >= mla_workspace_size(problem, num_shards, shard_id, top_k) bytes.
+ *  workspace   >= mla_workspace_size(problem, num_shards, shard_id, top_k) bytes
+ *              (never 0: it holds each shard's part of every list).
+ *
+ * The call first splits every list by owner shard (in list order) into the
+ * workspace, then each shard streams only its own part; partitions are cut for
+ * an even share, min(top_k, max_seq_len) / num_shards entries, so lists that
+ * crowd one shard stay correct but run longer.
  */
 mla_status_t mla_decode_sparse_dcp(const mla_problem_t *problem, const int32_t *indices,
                                    int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,

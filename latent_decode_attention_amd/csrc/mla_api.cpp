@@ -32,7 +32,8 @@ struct Plan {
   int kernel_rows;  // 128 or 64
   int units, splits, chunk, stream_len;
   int64_t grid;
-  size_t ws_o, ws_lse, ws_scale, ws_total;
+  int lists_q;  // sparse under DCP: per-shard lists kept per query token (Q) or shared (1)
+  size_t ws_o, ws_lse, ws_scale, ws_lists, ws_counts, ws_total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -73,7 +74,13 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
     return MLA_ERR_BAD_SHAPE;
   if (num_cus < 1) num_cus = kDefaultCus;
   int64_t L;
-  if (sparse) {
+  if (sparse && num_shards > 1) {
+    // Each shard streams its own part of the list (split off by
+    // partition_kernel); partitions are cut for an even share, and the last
+    // partition of a unit takes whatever a skewed list adds beyond it.
+    const int64_t valid = std::min<int64_t>(top_k, p->max_seq_len);
+    L = (valid + num_shards - 1) / num_shards;
+  } else if (sparse) {
     L = top_k;
   } else if (num_shards > 1) {
     L = 0;
@@ -110,10 +117,31 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
     const int64_t units = (int64_t)p->B * o->q_groups * shard_units;
     if (units > INT32_MAX) return false;
     o->units = (int)units;
+    int64_t max_splits = 1;
+    if (units < num_cus && tiles > 1) max_splits = std::min<int64_t>((num_cus + units - 1) / units, tiles);
+    // Partitions buy parallelism but their partial results must be written,
+    // read back and merged.  Take the count with the lowest estimated time:
+    // rounds of work-groups x (per-group fixed cost + tiles x per-tile cost),
+    // plus the merge at the bytes it moves (costs measured on MI355X; sharded
+    // outputs keep fp32 partials, others fp16 with 4 scales per row).
+    const double t_tile = R == 128 ? 4.0 : 2.4, t_fixed = 9.0;  // microseconds
+    const double part_row = num_shards > 1 ? kDv * 4.0 + 4 : kDv * 2.0 + 20;
+    const double out_row = num_shards > 1 ? kDv * 4.0 + 4 : kDv * 2.0 + 4;
+    const double rows = (double)p->B * p->Q * p->h_q * shard_units;
     int64_t splits = 1;
-    if (units < num_cus && tiles > 1) splits = std::min<int64_t>((num_cus + units - 1) / units, tiles);
+    double best = 0;
+    for (int64_t s = 1; s <= max_splits; ++s) {
+      const int64_t per = tiles > 0 ? (tiles + s - 1) / s : 1;
+      if (tiles > 0 && (tiles + per - 1) / per != s) continue;  // same cut as fewer partitions
+      const double rounds = std::ceil((double)units * s / num_cus);
+      double t = rounds * (t_fixed + per * t_tile);
+      if (s > 1) t += 2.0 + rows * (s * part_row + out_row) / 5.0e6;  // ~5 TB/s
+      if (s == 1 || t < best) {
+        best = t;
+        splits = s;
+      }
+    }
     const int64_t tiles_per_split = tiles > 0 ? (tiles + splits - 1) / splits : 1;
-    splits = tiles > 0 ? (tiles + tiles_per_split - 1) / tiles_per_split : 1;
     o->splits = (int)splits;
     o->chunk = (int)(tiles_per_split * kTile);
     o->grid = units * splits;
@@ -144,7 +172,15 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   } else {
     pl->ws_o = pl->ws_lse = pl->ws_scale = 0;
   }
-  pl->ws_total = pl->ws_o + pl->ws_lse + pl->ws_scale;
+  pl->lists_q = shared_list ? 1 : p->Q;
+  pl->ws_lists = pl->ws_counts = 0;
+  if (sparse && num_shards > 1) {
+    // Sized for one list per query token so that one size fits either layout.
+    const int64_t lists = (int64_t)p->B * p->Q * pl->shard_units;
+    pl->ws_lists = align256((size_t)(lists * top_k) * sizeof(int32_t));
+    pl->ws_counts = align256((size_t)lists * sizeof(int32_t));
+  }
+  pl->ws_total = pl->ws_o + pl->ws_lse + pl->ws_scale + pl->ws_lists + pl->ws_counts;
   return MLA_OK;
 }
 
@@ -210,6 +246,29 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
     a.part_f16 = out_fp32 ? 0 : 1;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sparse && num_shards > 1) {
+    char *ws = static_cast<char *>(workspace) + pl.ws_o + pl.ws_lse + pl.ws_scale;
+    PartitionArgs pa;
+    pa.indices = indices;
+    pa.stride_b = stride_b;
+    pa.stride_q = stride_q;
+    pa.seq_lens = p->seq_lens;
+    pa.top_k = top_k;
+    pa.B = p->B;
+    pa.lists_q = pl.lists_q;
+    pa.num_shards = num_shards;
+    pa.interleave = interleave;
+    pa.by_interleave = make_fastdiv((uint32_t)interleave);
+    pa.by_shards = make_fastdiv((uint32_t)num_shards);
+    pa.shard_base = a.shard_base;
+    pa.shard_units = pl.shard_units;
+    pa.lists = reinterpret_cast<int32_t *>(ws);
+    pa.counts = reinterpret_cast<int32_t *>(ws + pl.ws_lists);
+    if (launch_partition(pa, s) != hipSuccess) return MLA_ERR_LAUNCH;
+    a.indices = pa.lists;
+    a.idx_counts = pa.counts;
+    a.lists_q = pl.lists_q;
+  }
   if (launch_decode(a, pl.grid, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.splits > 1) {
     MergeArgs m;

@@ -191,15 +191,27 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
   u.shard = a.shard_base + su;
   u.S = uniform(a.seq_lens[u.b]);
   int L;
-  if constexpr (kMode == kSparseStream)
-    L = a.top_k;
-  else if constexpr (kMode == kShardStream)
+  u.idx_base = 0;
+  bool rest = false;  // the last partition also takes what the plan did not foresee
+  if constexpr (kMode == kSparseStream) {
+    if (a.idx_counts) {
+      // This shard's own list; its length is known only on the device.  The
+      // plan cuts partitions for an even share of the entries per shard.
+      const int64_t list = ((int64_t)u.b * a.lists_q + (a.lists_q > 1 ? u.q0 : 0)) * a.shard_units + su;
+      L = uniform(a.idx_counts[list]);
+      u.idx_base = uniform(list * a.top_k);
+      rest = u.split == a.splits - 1;
+    } else {
+      L = a.top_k;
+      u.idx_base = uniform((int64_t)u.b * a.idx_stride_b + (int64_t)u.q0 * a.idx_stride_q);
+    }
+  } else if constexpr (kMode == kShardStream) {
     L = shard_len(u.S, a.num_shards, a.interleave, u.shard);
-  else
+  } else {
     L = u.S > 0 ? u.S : 0;
+  }
   u.i0 = uniform(u.split * a.chunk);
-  u.i1 = uniform(min(L, u.i0 + a.chunk));
-  u.idx_base = kMode == kSparseStream ? uniform((int64_t)u.b * a.idx_stride_b + (int64_t)u.q0 * a.idx_stride_q) : 0;
+  u.i1 = uniform(rest ? L : min(L, u.i0 + a.chunk));
   u.bt = a.block_table + uniform((int64_t)u.b * a.max_blocks);
   return u;
 }
@@ -223,18 +235,12 @@ __device__ __forceinline__ int raw_block(const DecodeArgs &a, const Unit &u, int
   return u.bt[slot];
 }
 // Physical cache row of a token, or -1 when no query row of this group attends
-// it.  A sparse list under DCP keeps only the positions this shard holds,
-// floor(p / interleave) mod N = shard (the DCP page's interleaved placement,
-// §2.1.4.1); dense shard streams only ever produce such positions.
-template <int kMode>
+// it.  (Under DCP, streams hold only positions of their own shard: dense
+// streams by construction, sparse ones after partition_kernel.)
 __device__ __forceinline__ int token_row(const DecodeArgs &a, const Unit &u, int i, int p, int blk) {
   const int last = u.S - a.Q + u.q0 + a.q_per_group - 1;
-  bool ok = i < u.i1 && p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && blk >= 0 &&
-            blk < a.num_blocks;
-  if constexpr (kMode == kSparseStream) {
-    if (a.num_shards > 1)
-      ok = ok && ((unsigned)p / (unsigned)a.interleave) % (unsigned)a.num_shards == (unsigned)u.shard;
-  }
+  const bool ok = i < u.i1 && p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && blk >= 0 &&
+                  blk < a.num_blocks;
   return ok ? blk * a.block_size + (p & (a.block_size - 1)) : -1;
 }
 
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     __builtin_amdgcn_sched_barrier(0);
     after_blocks();
     __builtin_amdgcn_sched_barrier(0);
-    const int row0 = token_row<kMode>(a, u, u.i0 + plane, p0, b0);
+    const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
     copy_all(prepare_copy(sm.tile[0], a, wave, lane, row0));
     mask_cur = tile_mask(a, u, p0, row0);
   };
@@ -589,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       TileCopy next_copy;
       auto tile_step_work = [&](int step) {
         if (step == 0) {
-          row1 = token_row<kMode>(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
+          row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
           crow = copy_rows(row1, wave, lane);
         }
         if (step == 2) next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);
@@ -1104,6 +1110,47 @@ __global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWrite
   }
 }
 
+
+// Splitting top-k lists by DCP shard ("RFC: MsModeling 支持 Decode Context
+// Parallel 仿真", §2.1.4.1: position p lives on shard floor(p / I) mod N).  One
+// wave per (sequence, list, shard) scans the list in order and appends the
+// entries its shard owns, so every shard's list keeps the list's order and the
+// result does not depend on scheduling.  Negative entries (padding) and entries
+// at or past the sequence length are dropped here: no query token attends them.
+constexpr int kPartitionThreads = 256;
+constexpr int kPartitionBatch = 32;  // entries per lane per pass: 2048 entries in one round trip
+__global__ __launch_bounds__(kPartitionThreads) void partition_kernel(const PartitionArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t id = (int64_t)blockIdx.x * (kPartitionThreads / 64) + (threadIdx.x >> 6);
+  if (id >= (int64_t)a.B * a.lists_q * a.shard_units) return;  // whole waves leave
+  const int64_t bl = id / a.shard_units;
+  const int l = (int)(bl % a.lists_q), b = (int)(bl / a.lists_q);
+  const unsigned r = (unsigned)(a.shard_base + (int)(id % a.shard_units));
+  const int32_t *src = a.indices + (int64_t)b * a.stride_b + (int64_t)l * a.stride_q;
+  int32_t *dst = a.lists + id * a.top_k;
+  const int S = a.seq_lens[b];
+  int count = 0;
+  for (int base = 0; base < a.top_k; base += 64 * kPartitionBatch) {
+    int v[kPartitionBatch];
+#pragma unroll
+    for (int j = 0; j < kPartitionBatch; ++j)  // every load issued before the first use
+      v[j] = src[min(base + 64 * j + lane, a.top_k - 1)];
+#pragma unroll
+    for (int j = 0; j < kPartitionBatch; ++j) {
+      const int p = v[j];
+      const unsigned run = fastdiv((unsigned)p, a.by_interleave);
+      const unsigned owner = run - fastdiv(run, a.by_shards) * (unsigned)a.num_shards;
+      const bool mine = base + 64 * j + lane < a.top_k && p >= 0 && p < S && owner == r;
+      const unsigned long long m = __ballot(mine);
+      const int before =
+          __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      if (mine) dst[count + before] = p;
+      count += __popcll(m);
+    }
+  }
+  if (lane == 0) a.counts[id] = count;
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
@@ -1119,6 +1166,14 @@ hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t strea
     if (wide) hipLaunchKernelGGL((decode_kernel<kDenseStream, 128>), g, b, 0, stream, args);
     else hipLaunchKernelGGL((decode_kernel<kDenseStream, 64>), g, b, 0, stream, args);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_partition(const PartitionArgs &args, hipStream_t stream) {
+  const int64_t waves = (int64_t)args.B * args.lists_q * args.shard_units;
+  const int64_t per_block = kPartitionThreads / 64;
+  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)((waves + per_block - 1) / per_block)),
+                     dim3(kPartitionThreads), 0, stream, args);
   return hipGetLastError();
 }
 

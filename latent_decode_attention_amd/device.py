@@ -46,6 +46,8 @@ def run(d: DeviceWorkload, out_dtype=torch.bfloat16, shard_id: Optional[int] = N
                                     d.indices if indices is None else indices, scale=w.scale,
                                     max_seq_len=w.max_seq_len, top_k=w.top_k,
                                     index_stride_b=w.index_stride_b, index_stride_q=w.index_stride_q,
+                                    num_shards=w.num_shards, interleave=w.interleave,
+                                    shard_id=-1 if shard_id is None else shard_id,
                                     out_dtype=out_dtype, workspace=workspace, stream=stream)
     if w.num_shards > 1:
         return md.mla_decode_dense(d.q, d.kv, d.block_table, d.seq_lens, scale=w.scale,

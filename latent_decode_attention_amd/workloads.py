@@ -240,6 +240,13 @@ def config_dense_32k(seed: int = 1006) -> Workload:
     return make_workload("dense_paged_b32_h128_s32768", 32, 1, 128, [32768] * 32, 64, seed)
 
 
+def config_sparse_dcp(seed: int = 1007) -> Workload:
+    """Sparse top-k under DCP: the split-KV shape (B=8 Q=1 h_q=128 S=131072, 8
+    shards interleaved by 64 tokens) attending a top_k=2048 list per sequence."""
+    return make_workload("sparse_dcp_b8_h128_s131072_top2048_n8_i64", 8, 1, 128, [131072] * 8, 64, seed,
+                         top_k=2048, num_shards=8, interleave=64)
+
+
 CONFIGS = {
     1: config_tiny,
     2: config_dense_paged,
@@ -247,6 +254,7 @@ CONFIGS = {
     4: config_split_kv,
     5: config_mtp,
     6: config_dense_32k,
+    7: config_sparse_dcp,
 }
 
 

@@ -148,15 +148,25 @@ def test_plan_shards_cover_their_positions(S, N, I):
 
 
 def test_plan_sparse_shards():
-    # sparse x DCP: every shard streams the whole list (the shard keeps its own entries)
-    pl = plan(problem(B=8, max_seq_len=131072, max_blocks=2048), top_k=2048, num_shards=8, interleave=64,
-              shard_id=-1)
-    assert pl["stream_len"] == 2048
+    # sparse x DCP: each shard streams its own part of the list, planned as an
+    # even share of min(top_k, S) entries; the workspace holds the split lists
+    pr = problem(B=8, max_seq_len=131072, max_blocks=2048)
+    pl = plan(pr, top_k=2048, num_shards=8, interleave=64, shard_id=-1)
+    assert pl["stream_len"] == 256
     assert pl["units"] == 8 * 8 * (128 // pl["rows_per_group"])  # sequences x shards x head chunks
     assert pl["grid"] == pl["units"] * pl["splits"]
-    one = plan(problem(B=8, max_seq_len=131072, max_blocks=2048), top_k=2048, num_shards=8, interleave=64,
-               shard_id=3)
-    assert one["stream_len"] == 2048 and one["units"] == 8 * (128 // one["rows_per_group"])
+    assert pl["splits"] * pl["chunk"] >= 256
+    lists = 8 * 1 * 8 * 2048 * 4
+    assert pl["workspace_bytes"] >= lists
+    assert md.mla_workspace_size(pr, 8, -1, 2048) == pl["workspace_bytes"]
+    one = plan(pr, top_k=2048, num_shards=8, interleave=64, shard_id=3)
+    assert one["stream_len"] == 256 and one["units"] == 8 * (128 // one["rows_per_group"])
+    assert md.mla_workspace_size(pr, 8, 3, 2048) >= 8 * 2048 * 4
+    # short sequences bound the share: S = 1000 < top_k, 3 shards -> 334
+    short = plan(problem(B=8, max_seq_len=1000, max_blocks=16), top_k=2048, num_shards=3, interleave=7)
+    assert short["stream_len"] == 334
+    # per-token lists (Q = 2) are sized for as well
+    assert md.mla_workspace_size(problem(B=8, Q=2, max_seq_len=4096, max_blocks=64), 4, -1, 512) >= 8 * 2 * 4 * 512 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
