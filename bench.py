@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, TFLOP/s
 METRIC = "sparse/dense MLA decode KV-token·heads/s at 1 GPU; % of HBM/MFMA roofline"
 KERNEL_SOURCES = [os.path.join(ROOT, "latent_decode_attention_amd", "csrc", f)
-                  for f in ("mla_kernels.hip", "mla_api.cpp", "mla_internal.h")]
+                  for f in ("mla_kernels.hip", "mla_api.cpp", "mla_internal.h", "mla_fastdiv.h")]
 
 
 def kernel_hash() -> str:
@@ -83,8 +83,9 @@ def algorithmic_work(w, indices_list=None):
 
 
 def stored_traffic(workload_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
-    kernel sources have not changed since the counters were taken."""
+    """HBM bytes per call (every kernel the call launches) from the committed
+    rocprofv3 counter summary, if the kernel sources have not changed since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
@@ -174,7 +175,8 @@ def run_kv_write(args, torch, md, W, dev):
         "config": {"workload": f"kv_write_t{T}_slots{num_slots}", "T": T, "num_slots": num_slots,
                    "stored_rows_mean": stored, "rotating_input_sets": sets},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kv_write_kernel",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(f"kv_write_t{T}_slots{num_slots}"),
+                     "kernel": "kv_write_kernel",
                      "launch_ms": ms, "algorithmic_bytes": nbytes},
     }
     print(f"[bench] kv_write {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s algorithmic = {gbs / HBM_PEAK_GBS:.3f} "

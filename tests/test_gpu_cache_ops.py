@@ -57,3 +57,35 @@ def test_kv_write_at_the_bench_size():
     x = W.make_kv_write_inputs(32768, 65536, seed=1007)
     kv = _cache(65536, 1008)
     assert np.array_equal(_run(kv, x), cache_ops.kv_write(kv, x.rows, x.slots))
+
+
+def test_decode_reads_the_rows_the_write_stored():
+    # The last 40 positions of each sequence are overwritten with NaN, then stored
+    # back by mla_kv_write through slots block_table[b, p / bs] * bs + p % bs (two
+    # interleaved DCP shards, each storing its own tokens): the decode of the
+    # restored cache must match the oracle on the original cache.
+    import oracle
+    from latent_decode_attention_amd.device import upload, run
+    w = W.make_workload("kvw_decode", 2, 1, 16, [300, 170], 16, seed=21)
+    ref_o, ref_l = oracle.dense(w)
+    bs = w.block_size
+    flat = w.kv.reshape(-1, W.D_QK)
+    rows, slots, pos = [], [], []
+    for b, S in enumerate(w.seq_lens):
+        for p in range(S - 40, S):
+            slot = int(w.block_table[b, p // bs]) * bs + p % bs
+            rows.append(flat[slot].copy())
+            slots.append(slot)
+            pos.append(p)
+    rows, slots, pos = np.stack(rows), np.array(slots, np.int32), np.array(pos, np.int32)
+    w.kv = w.kv.copy()
+    w.kv.reshape(-1, W.D_QK)[slots] = W.BF16_NAN
+    d = upload(w)
+    for r in range(2):
+        md.mla_kv_write(_dev(rows, np.int16).view(torch.bfloat16), _dev(slots, np.int32),
+                        d.kv.view(-1, W.D_QK), positions=_dev(pos, np.int32), num_shards=2, interleave=16,
+                        shard_id=r)
+    out, lse = run(d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy().astype(np.float64).reshape(ref_o.shape) - ref_o).max() <= 1e-2
+    assert np.abs(lse.cpu().numpy().astype(np.float64).reshape(ref_l.shape) - ref_l).max() <= 1e-3
