@@ -316,3 +316,31 @@ def make_kv_write_inputs(T: int, num_slots: int, seed: int, skip_frac: float = 0
         slots[far] = num_slots + np.arange(k, dtype=np.int32)
     positions = g_pos.permutation(T).astype(np.int32)
     return KvWriteInputs(rows=rows, slots=slots, positions=positions, num_slots=num_slots)
+
+
+@dataclass
+class TopkInputs:
+    """Seeded indexer scores for the top-k selection: float32 [B, Q, max_len]."""
+    scores: np.ndarray
+    seq_lens: np.ndarray   # int32 [B]
+    top_k: int
+
+
+def make_topk_scores(B: int, Q: int, seq_lens, top_k: int, seed: int, zero_frac: float = 0.25,
+                     max_len: int = 0) -> TopkInputs:
+    """N(0,1) scores rounded to bf16 precision (so equal scores occur, as from bf16
+    indexer arithmetic), a `zero_frac` share set to exactly 0 (a ReLU-weighted
+    score's zeros: long runs of ties), and +inf past each row's causal length
+    S_b - Q + q + 1, so that a read beyond the row would be selected and seen."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (B,)
+    max_len = max_len or int(seq_lens.max(initial=1))
+    g_val, g_zero = _children(seed, 2)
+    x = g_val.standard_normal((B, Q, max_len), dtype=np.float32)
+    s = bf16_bits_to_f32(f32_to_bf16_bits(x)).reshape(B, Q, max_len)
+    s[g_zero.random((B, Q, max_len)) < zero_frac] = 0.0
+    for b in range(B):
+        for q in range(Q):
+            L = min(max(int(seq_lens[b]) - Q + q + 1, 0), max_len)
+            s[b, q, L:] = np.inf
+    return TopkInputs(scores=np.ascontiguousarray(s, dtype=np.float32), seq_lens=seq_lens, top_k=top_k)
