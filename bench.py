@@ -198,6 +198,63 @@ def run_kv_write(args, torch, md, W, dev):
     print(json.dumps(rec), flush=True)
 
 
+def run_topk(args, torch, md, W, dev):
+    """Indexer top-k selection at the headline sparse shape: B = 32 rows of S =
+    32768 fp32 scores, top 2048 each.  Each call reads a different one of 72
+    score sets (302 MB in all, each a rolled copy of one seeded set) so the
+    Infinity Cache cannot serve them.  Bytes = every score once (4 B) + the
+    selected positions (4 B each) + seq_lens."""
+    B, S, k, sets = 32, 32768, 2048, 72
+    x = W.make_topk_scores(B, 1, [S] * B, k, seed=1009)
+    base = torch.from_numpy(x.scores).to(dev)
+    scores = [torch.roll(base, shifts=977 * r, dims=2).contiguous() for r in range(sets)]
+    seq = torch.from_numpy(x.seq_lens).to(dev)
+    out = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        md.mla_topk_select(scores[i % sets], seq, k, out=out, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    ranked = B * S
+    nbytes = ranked * 4 + B * k * 4 + B * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    name = f"topk_b{B}_s{S}_k{k}"
+    rec = {
+        "metric": "indexer top-k selection, scores ranked/s at 1 GPU; % of HBM roofline",
+        "value": ranked / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "B": B, "Q": 1, "seq_len": S, "top_k": k, "rotating_input_sets": sets},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(name), "kernel": "topk_kernel",
+                     "launch_ms": ms, "algorithmic_bytes": nbytes},
+    }
+    print(f"[bench] topk {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s algorithmic = {gbs / HBM_PEAK_GBS:.3f} "
+          f"of HBM peak", file=sys.stderr, flush=True)
+    rec["cpu_baseline"] = None
+    if args.cpu_seconds > 0:
+        from oracle import topk
+        t0, rows = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            b = rows % B
+            topk.select_row(x.scores[b, 0], k)
+            rows += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": rows * S / dt, "unit": "scores/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} rows of {S} scores of the same workload, numpy, {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,7 +264,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="distinct input sets cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
-    ap.add_argument("--op", default="decode", choices=["decode", "kv_write"],
+    ap.add_argument("--op", default="decode", choices=["decode", "kv_write", "topk"],
                     help="decode: the attention call (default); kv_write: the latent-cache write "
                          "through slot_mapping (32768 prefill tokens into a 262144-slot cache)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -237,6 +294,9 @@ def main():
         return
     if args.op == "kv_write":
         run_kv_write(args, torch, md, W, dev)
+        return
+    if args.op == "topk":
+        run_topk(args, torch, md, W, dev)
         return
     t0 = time.time()
     w = W.CONFIGS[args.config]()

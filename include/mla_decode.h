@@ -228,6 +228,33 @@ mla_status_t mla_kv_write(const void *rows, const int32_t *slot_mapping, int64_t
                           int64_t num_slots, const int32_t *positions, int32_t num_shards,
                           int32_t interleave, int32_t shard_id, void *stream);
 
+/*
+ * Top-k selection of indexer scores: the positions a sparse decode attends.
+ * The DSA indexer picks the 2048 best-scored positions per query token ("vllm-
+ * ascend PR #18870 解读：FlashComm1 的'假开启'与 SP 归位", §4.5; "RFC: Context
+ * Parallel Modeling for DeepSeek-Style Attention", §3.3 models this top-k side
+ * of the fused indexer on its own); computing the scores needs the indexer's
+ * trained weights and is not part of this library.
+ *
+ * Row (b, q) ranks positions p in [0, L) with L = min(max(seq_lens[b] - Q + q + 1,
+ * 0), max_len) (query token q attends up to its own position) by the score
+ * scores[b * stride_b + q * stride_q + p]: a larger score ranks higher, NaN
+ * ranks below every number, -0 equals +0, and equal scores rank by position,
+ * lower first.  out[b, q, 0 .. top_k) receives the min(top_k, L) best positions
+ * in ascending order, then -1: directly the index list of mla_decode_sparse with
+ * index_stride_b = Q * top_k and index_stride_q = top_k.  The result is unique
+ * and bit-reproducible.
+ *
+ *  scores    device, fp32; each row readable for p < L(b, q)
+ *  stride_b, stride_q  elements, >= 0
+ *  seq_lens  device, int32 [B]
+ *  B >= 1;  Q in 1..16;  max_len >= 1;  top_k in 1..65536
+ *  out       device, int32 [B, Q, top_k]
+ */
+mla_status_t mla_topk_select(const float *scores, int64_t stride_b, int64_t stride_q,
+                             const int32_t *seq_lens, int32_t B, int32_t Q, int32_t max_len,
+                             int32_t top_k, int32_t *out, void *stream);
+
 /* Static, human-readable name of a status. */
 const char *mla_status_string(mla_status_t status);
 

@@ -352,6 +352,26 @@ mla_status_t mla_decode_sparse_dcp(const mla_problem_t *problem, const int32_t *
              shard_id, out, true, lse, workspace, workspace_bytes, stream);
 }
 
+mla_status_t mla_topk_select(const float *scores, int64_t stride_b, int64_t stride_q,
+                             const int32_t *seq_lens, int32_t B, int32_t Q, int32_t max_len,
+                             int32_t top_k, int32_t *out, void *stream) {
+  if (!scores || !seq_lens || !out) return MLA_ERR_NULL_POINTER;
+  if (B < 1 || Q < 1 || Q > 16 || max_len < 1 || top_k < 1 || top_k > kMaxTopK || stride_b < 0 ||
+      stride_q < 0 || (int64_t)B * Q > INT32_MAX)
+    return MLA_ERR_BAD_SHAPE;
+  TopkArgs a;
+  a.scores = scores;
+  a.stride_b = stride_b;
+  a.stride_q = stride_q;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.Q = Q;
+  a.max_len = max_len;
+  a.top_k = top_k;
+  a.out = out;
+  return launch_topk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t n,
                            int64_t rows, int32_t d_v, void *out, mla_dtype_t out_dtype,
                            float *lse_out, void *stream) {

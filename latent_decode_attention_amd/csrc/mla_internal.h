@@ -96,9 +96,22 @@ struct PartitionArgs {
   int32_t *counts;
 };
 
+// Top-k selection over indexer scores: row (b, q) holds the scores of positions
+// [0, L) with L = clamp(seq_lens[b] - Q + q + 1, 0, max_len) at
+// scores[b * stride_b + q * stride_q + p]; out [B, Q, top_k] receives the
+// selected positions in ascending order, -1 padded.
+struct TopkArgs {
+  const float *scores;
+  int64_t stride_b, stride_q;
+  const int32_t *seq_lens;
+  int32_t B, Q, max_len, top_k;
+  int32_t *out;
+};
+
 // Enqueue the kernels; return the HIP status of the launch.
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream);
 hipError_t launch_partition(const PartitionArgs &args, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs &args, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs &args, hipStream_t stream);
 

@@ -1151,6 +1151,350 @@ __global__ __launch_bounds__(kPartitionThreads) void partition_kernel(const Part
   if (lane == 0) a.counts[id] = count;
 }
 
+// ---- Top-k selection of the indexer's scores (the positions a sparse decode
+// attends: "vllm-ascend PR #18870 解读：FlashComm1 的'假开启'与 SP 归位", §4.5,
+// top-2048 per query token).  Ranking: larger score first, NaN below every
+// number, -0 = +0, equal scores by lower position; the chosen positions are
+// written in ascending order and the row is padded with -1.
+//
+// One work-group per row.  Each score maps to a 32-bit key whose unsigned order
+// is that ranking (positions break the remaining ties).  Four passes, one per
+// 8-bit digit from the top, histogram the digit among keys that match the
+// digits chosen so far and pick the digit at which the count from the top
+// reaches the number still to choose: after them the exact key T of the last
+// chosen element is known, and how many of the keys equal to T to take.  A last
+// pass marks the keys above T and the keys equal to T in two LDS bitmaps (a bit
+// per position); each thread takes two words of each, and one block-wide prefix
+// sum of their counts gives every word its output offset (the chosen keys above
+// T before it, plus the ties before it up to the number taken).  The positions
+// are staged in LDS in order and written out coalesced.
+//
+// Layout: 512 threads; a segment of 32768 positions is 16 slabs of 2048, and
+// thread t holds positions 4t .. 4t+3 of every slab (one 16-byte load per
+// slab, coalesced across the wave), as keys in registers for all passes.
+// Rows longer than one segment are taken segment by segment, reloaded per
+// pass.
+//
+// A wave's LDS atomic costs about the same however few of its lanes take
+// part, so the passes of a row that fits one segment work on short lists:
+// each thread's m-th largest key, m = ceil(k / 512), bounds T from below by
+// the smallest of them (at least 512 m >= k keys reach it); every wave copies
+// its keys at or above that bound into its own LDS list, counts the list, and
+// after each pass keeps only the keys that match the digits chosen so far.
+constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkSlabs = 16;                                 // slabs of 2048 positions per segment
+constexpr int kTopkSlabLen = 4 * kTopkThreads;
+constexpr int kTopkPerThread = 4 * kTopkSlabs;                 // keys held per thread
+constexpr int kTopkSeg = kTopkThreads * kTopkPerThread;        // 32768 positions per segment
+constexpr int kTopkMapWords = kTopkSeg / 32;                  // bitmap words per segment
+constexpr int kTopkMaxM = 4;                                   // largest m the lower bound is formed for
+
+__device__ __forceinline__ uint32_t rank_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (x != x) return 1u;          // NaN: below every number (-inf maps to 0x007fffff)
+  if ((u << 1) == 0u) u = 0u;     // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the work-group; `total` receives the sum.  The
+// trailing barrier frees `part`.
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *part, uint32_t &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) part[wave] = x;
+  __syncthreads();
+  uint32_t base = 0, sum = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) {
+    const uint32_t c = part[i];
+    base += i < wave ? c : 0u;
+    sum += c;
+  }
+  __syncthreads();
+  total = sum;
+  return base + x - v;
+}
+// The n lowest set bits of x.
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t x, uint32_t n) {
+  if (n >= (uint32_t)__popc(x)) return x;
+  uint32_t r = 0;
+  for (uint32_t i = 0; i < n; ++i) {
+    r |= x & (0u - x);
+    x &= x - 1u;
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
+  __shared__ uint32_t hist[kTopkWaves][256];
+  __shared__ uint32_t cand[kTopkWaves][64 * kTopkPerThread];  // each wave's candidate keys
+  __shared__ uint32_t gt_map[kTopkMapWords], eq_map[kTopkMapWords];
+  __shared__ uint32_t total[256];
+  __shared__ uint32_t part[kTopkWaves];
+  __shared__ uint32_t pick[2][2];  // per pass parity: chosen digit, count of keys above it
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const int b = row / a.Q, q = row % a.Q;
+  const float *src = a.scores + (int64_t)b * a.stride_b + (int64_t)q * a.stride_q;
+  int32_t *dst = a.out + (int64_t)row * a.top_k;
+  const int L = min(max(a.seq_lens[b] - a.Q + q + 1, 0), a.max_len);
+  const int k = min(a.top_k, L);
+  for (int i = k + tid; i < a.top_k; i += kTopkThreads) dst[i] = -1;
+  if (k == L) {  // every position is chosen
+    for (int i = tid; i < L; i += kTopkThreads) dst[i] = i;
+    return;
+  }
+  // key 0 = past the row: below every score (whose keys are >= 1).  Every
+  // load is issued unconditionally from a clamped address and the keys of
+  // positions past the row are set afterwards, so all loads of a segment are in
+  // flight together: 16-byte loads when the row is 16-byte aligned and a
+  // multiple of 4 long (a load then never straddles the row's end), else
+  // 4-byte loads.
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (L & 3) == 0;
+  const bool resident = L <= kTopkSeg;
+  uint32_t key[kTopkPerThread];
+  auto load = [&](int seg) {
+    if (vec) {
+      float4 f[kTopkSlabs];
+#pragma unroll
+      for (int j = 0; j < kTopkSlabs; ++j)
+        f[j] = *reinterpret_cast<const float4 *>(src + min(seg + kTopkSlabLen * j + 4 * tid, L - 4));
+#pragma unroll
+      for (int j = 0; j < kTopkSlabs; ++j) {
+        const bool in = seg + kTopkSlabLen * j + 4 * tid < L;  // all four or none
+        key[4 * j] = in ? rank_key(f[j].x) : 0u;
+        key[4 * j + 1] = in ? rank_key(f[j].y) : 0u;
+        key[4 * j + 2] = in ? rank_key(f[j].z) : 0u;
+        key[4 * j + 3] = in ? rank_key(f[j].w) : 0u;
+      }
+    } else {
+      float f[kTopkPerThread];
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread; ++j)
+        f[j] = src[min(seg + kTopkSlabLen * (j >> 2) + 4 * tid + (j & 3), L - 1)];
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread; ++j)
+        key[j] = seg + kTopkSlabLen * (j >> 2) + 4 * tid + (j & 3) < L ? rank_key(f[j]) : 0u;
+    }
+  };
+  if (resident) load(0);
+
+  // Lower bound of T (keys below it are never counted) and the largest key.
+  uint32_t lo = 1u, hi = 0xffffffffu;
+  const int m = (k + kTopkThreads - 1) / kTopkThreads;
+  if (resident && m <= kTopkMaxM) {
+    uint32_t t[kTopkMaxM] = {0u, 0u, 0u, 0u};  // this thread's largest keys, descending
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread; ++j) {
+      uint32_t x = key[j];
+#pragma unroll
+      for (int r = 0; r < kTopkMaxM; ++r) {
+        const uint32_t hi = max(t[r], x);
+        x = min(t[r], x);
+        t[r] = hi;
+      }
+    }
+    const uint32_t mth = m == 1 ? t[0] : m == 2 ? t[1] : m == 3 ? t[2] : t[3];
+    // threads with fewer than m keys (mth == 0) do not take part
+    uint32_t mn = mth ? mth : 0xffffffffu, cnt = mth ? 1u : 0u, mx = t[0];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor(mn, o, 64));
+      mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+      cnt += __shfl_xor(cnt, o, 64);
+    }
+    if (lane == 0) {
+      total[wave] = mn;
+      total[kTopkWaves + wave] = cnt;
+      total[2 * kTopkWaves + wave] = mx;
+    }
+    __syncthreads();
+    uint32_t bmin = 0xffffffffu, bcnt = 0, bmax = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) {
+      bmin = min(bmin, total[i]);
+      bcnt += total[kTopkWaves + i];
+      bmax = max(bmax, total[2 * kTopkWaves + i]);
+    }
+    __syncthreads();
+    if (bcnt * (uint32_t)m >= (uint32_t)k) lo = bmin;
+    hi = bmax;
+  }
+
+  // This wave's list: its keys >= lo (resident rows only), in any order.
+  uint32_t n = 0;  // wave-uniform length
+  auto keep_list = [&](auto keep) {  // in place: a chunk is read before any write reaches it
+    uint32_t m2 = 0;
+    for (uint32_t base = 0; base < n; base += 64) {
+      const uint32_t i = base + lane;
+      const uint32_t kk = cand[wave][min(i, n - 1)];
+      const bool in = i < n && keep(kk);
+      const unsigned long long bm = __ballot(in);
+      if (in)
+        cand[wave][m2 + __builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, 0u))] = kk;
+      m2 += __popcll(bm);
+    }
+    n = m2;
+  };
+  if (resident) {
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread; ++j) {
+      const bool in = key[j] >= lo;
+      const unsigned long long bm = __ballot(in);
+      if (in)
+        cand[wave][n + __builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, 0u))] = key[j];
+      n += __popcll(bm);
+    }
+  }
+
+  // Pass 1 over few top bytes: when the keys from lo to hi span at most 8
+  // top-byte values, per-lane counters and a wave sum replace the atomics
+  // (whose lanes would mostly hit the same few words).
+  const uint32_t base8 = lo >> 24;
+  const bool narrow = resident && (hi >> 24) - base8 < 8u;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) (&hist[0][0])[tid + i * kTopkThreads] = 0u;
+  __syncthreads();
+  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
+  for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
+    // hist[] is zero here (cleared where it was last summed)
+    if (resident && pass == 0 && narrow) {
+      uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      for (uint32_t i = lane; i < n; i += 64) {
+        const uint32_t d = (cand[wave][i] >> 24) - base8;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) c[r] += d == (uint32_t)r;
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) c[r] += __shfl_xor(c[r], o, 64);
+      }
+      if (lane < 8) {
+        uint32_t v = c[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) v = lane == r ? c[r] : v;
+        if (base8 + lane < 256u) hist[wave][base8 + lane] = v;
+      }
+    } else if (resident) {
+      for (uint32_t i = lane; i < n; i += 64) atomicAdd(&hist[wave][(cand[wave][i] >> shift) & 255u], 1u);
+    } else {
+      for (int seg = 0; seg < L; seg += kTopkSeg) {
+        load(seg);
+#pragma unroll
+        for (int j = 0; j < kTopkPerThread; ++j) {
+          const uint32_t kk = key[j];
+          if (kk != 0u && (kk & mask) == prefix) atomicAdd(&hist[wave][(kk >> shift) & 255u], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int c = 0; c < kTopkWaves; ++c) {
+        t += hist[c][tid];
+        hist[c][tid] = 0u;
+      }
+      total[tid] = t;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // Lane l owns digits 4l .. 4l+3.  Count above its digits = the sum over
+      // higher lanes; then walk its own digits downwards.
+      uint32_t c[4], own = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = total[4 * lane + j];
+        own += c[j];
+      }
+      uint32_t x = own;  // inclusive sum from the top lane down
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(x, o, 64);
+        if (lane + o < 64) x += y;
+      }
+      uint32_t above = x - own;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (above < remaining && remaining <= above + c[j]) {
+          pick[pass & 1][0] = (uint32_t)(4 * lane + j);
+          pick[pass & 1][1] = above;
+        }
+        above += c[j];
+      }
+    }
+    __syncthreads();
+    prefix |= pick[pass & 1][0] << shift;
+    mask |= 255u << shift;
+    remaining -= pick[pass & 1][1];
+    if (resident && shift > 0) keep_list([&](uint32_t kk) { return (kk & mask) == prefix; });
+  }
+  // prefix is now the key T of the last element chosen; `remaining` of the keys
+  // equal to T are taken, lowest positions first.
+  const bool staged = k <= kTopkSeg;  // positions staged in LDS (the lists are done)
+  uint32_t *stage = &cand[0][0];
+  uint32_t above_seen = 0, equal_seen = 0;
+  for (int seg = 0; seg < L; seg += kTopkSeg) {
+    if (!resident) load(seg);
+#pragma unroll
+    for (int i = 0; i < kTopkMapWords / kTopkThreads; ++i) {
+      gt_map[tid + i * kTopkThreads] = 0u;
+      eq_map[tid + i * kTopkThreads] = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTopkSlabs; ++j) {
+      uint32_t g = 0, e = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        g |= (uint32_t)(key[4 * j + c] > prefix) << c;
+        e |= (uint32_t)(key[4 * j + c] == prefix) << c;
+      }
+      const int w = (kTopkSlabLen * j + 4 * tid) >> 5, sh = (4 * tid) & 31;
+      if (g) atomicOr(&gt_map[w], g << sh);
+      if (e) atomicOr(&eq_map[w], e << sh);
+    }
+    __syncthreads();
+    const int w0 = 2 * tid;
+    const uint32_t g0 = gt_map[w0], g1 = gt_map[w0 + 1], e0 = eq_map[w0], e1 = eq_map[w0 + 1];
+    uint32_t sums;
+    const uint32_t before = block_exclusive_sum((uint32_t)(__popc(g0) + __popc(g1)) |
+                                                    ((uint32_t)(__popc(e0) + __popc(e1)) << 16), part, sums);
+    uint32_t above_before = above_seen + (before & 0xffffu), eq_before = equal_seen + (before >> 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t g = h ? g1 : g0, e = h ? e1 : e0;
+      const uint32_t take = remaining > eq_before ? remaining - eq_before : 0u;
+      uint32_t sel = g | lowest_bits(e, take);
+      uint32_t o = above_before + min(eq_before, remaining);
+      const int p0 = seg + 32 * (w0 + h);
+      while (sel) {
+        const int bit = __ffs(sel) - 1;
+        if (o < (uint32_t)k) {
+          if (staged) stage[o] = p0 + bit;
+          else dst[o] = p0 + bit;
+        }
+        ++o;
+        sel &= sel - 1u;
+      }
+      above_before += __popc(g);
+      eq_before += __popc(e);
+    }
+    above_seen += sums & 0xffffu;
+    equal_seen += sums >> 16;
+    __syncthreads();  // the bitmaps are cleared for the next segment
+  }
+  if (staged)
+    for (int i = tid; i < k; i += kTopkThreads) dst[i] = stage[i];
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
@@ -1174,6 +1518,12 @@ hipError_t launch_partition(const PartitionArgs &args, hipStream_t stream) {
   const int64_t per_block = kPartitionThreads / 64;
   hipLaunchKernelGGL(partition_kernel, dim3((unsigned)((waves + per_block - 1) / per_block)),
                      dim3(kPartitionThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs &args, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((int64_t)args.B * args.Q)), dim3(kTopkThreads), 0, stream,
+                     args);
   return hipGetLastError();
 }
 

@@ -68,9 +68,11 @@ def _load() -> ctypes.CDLL:
     lib.mla_merge_lse.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp, vp]
     lib.mla_merge_lse.restype = ctypes.c_int
     lib.mla_kv_write.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, vp]
+    lib.mla_kv_write.restype = ctypes.c_int
     lib.mla_decode_sparse_dcp.argtypes = [P, vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.mla_decode_sparse_dcp.restype = ctypes.c_int
-    lib.mla_kv_write.restype = ctypes.c_int
+    lib.mla_topk_select.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, vp, vp]
+    lib.mla_topk_select.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_plan_query.argtypes = [P, i32, i32, i32, i32, i64, i32, ctypes.POINTER(Plan)]
@@ -266,3 +268,23 @@ def mla_kv_write(rows: torch.Tensor, slot_mapping: torch.Tensor, kv: torch.Tenso
     _check(lib.mla_kv_write(_ptr(rows), _ptr(slot_mapping), T, _ptr(kv), kv.numel() // 576, _ptr(positions),
                             num_shards, interleave, shard_id, _stream(stream)))
     return kv
+
+
+def mla_topk_select(scores: torch.Tensor, seq_lens: torch.Tensor, top_k: int, *,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Top-k positions of indexer scores [B, Q, max_len] fp32 (rows stop at the causal
+    limit seq_lens[b] - Q + q + 1): int32 [B, Q, top_k], ascending, -1 padded."""
+    if scores.dtype != torch.float32 or scores.dim() != 3 or not scores.is_cuda or scores.stride(2) != 1:
+        raise TypeError("scores must be a float32 GPU tensor [B, Q, max_len] with unit last stride")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous() or not seq_lens.is_cuda:
+        raise TypeError("seq_lens must be a contiguous int32 GPU tensor")
+    B, Q, max_len = scores.shape
+    if seq_lens.numel() != B:
+        raise TypeError("seq_lens must have B entries")
+    if out is None:
+        out = torch.empty((B, Q, top_k), dtype=torch.int32, device=scores.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (B, Q, top_k) or not out.is_contiguous():
+        raise TypeError("out must be a contiguous int32 tensor [B, Q, top_k]")
+    _check(lib.mla_topk_select(_ptr(scores), scores.stride(0), scores.stride(1), _ptr(seq_lens), B, Q, max_len,
+                               top_k, _ptr(out), _stream(stream)))
+    return out

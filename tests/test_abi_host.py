@@ -210,3 +210,15 @@ def test_kv_write_argument_checks(args, status):
     a.update(args)
     assert lib.mla_kv_write(a["rows"], a["slots"], a["T"], a["kv"], a["num_slots"], a["positions"],
                             a["num_shards"], a["interleave"], a["shard_id"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scores=None), 1), (dict(seq_lens=None), 1), (dict(out=None), 1), (dict(B=0), 2), (dict(Q=0), 2),
+    (dict(Q=17), 2), (dict(max_len=0), 2), (dict(top_k=0), 2), (dict(top_k=65537), 2), (dict(stride_b=-1), 2),
+    (dict(stride_q=-1), 2),
+])
+def test_topk_argument_checks(kw, status):
+    a = dict(scores=FAKE, stride_b=4096, stride_q=2048, seq_lens=FAKE, B=2, Q=2, max_len=2048, top_k=64, out=FAKE)
+    a.update(kw)
+    assert lib.mla_topk_select(a["scores"], a["stride_b"], a["stride_q"], a["seq_lens"], a["B"], a["Q"],
+                               a["max_len"], a["top_k"], a["out"], None) == status
