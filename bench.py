@@ -200,11 +200,12 @@ def run_kv_write(args, torch, md, W, dev):
 
 def run_topk(args, torch, md, W, dev):
     """Indexer top-k selection at the headline sparse shape: B = 32 rows of S =
-    32768 fp32 scores, top 2048 each.  Each call reads a different one of 72
-    score sets (302 MB in all, each a rolled copy of one seeded set) so the
-    Infinity Cache cannot serve them.  Bytes = every score once (4 B) + the
-    selected positions (4 B each) + seq_lens."""
-    B, S, k, sets = 32, 32768, 2048, 72
+    32768 fp32 scores (--topk-batch changes B), top 2048 each.  Each call reads
+    a different one of the score sets (about 300 MB in all, each a rolled copy
+    of one seeded set) so the Infinity Cache cannot serve them.  Bytes = every
+    score once (4 B) + the selected positions (4 B each) + seq_lens."""
+    B, S, k = args.topk_batch, 32768, 2048
+    sets = max(2, (300 << 20) // (B * S * 4))
     x = W.make_topk_scores(B, 1, [S] * B, k, seed=1009)
     base = torch.from_numpy(x.scores).to(dev)
     scores = [torch.roll(base, shifts=977 * r, dims=2).contiguous() for r in range(sets)]
@@ -264,9 +265,11 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="distinct input sets cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--topk-batch", type=int, default=32, help="rows of the top-k workload (--op topk)")
     ap.add_argument("--op", default="decode", choices=["decode", "kv_write", "topk"],
                     help="decode: the attention call (default); kv_write: the latent-cache write "
-                         "through slot_mapping (32768 prefill tokens into a 262144-slot cache)")
+                         "through slot_mapping (32768 prefill tokens into a 262144-slot cache); "
+                         "topk: the indexer's top-2048 selection over 32768 scores per row")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (the known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
