@@ -993,7 +993,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
 // lane then forms the maximum, the weights and their sum itself, in index
 // order, with no cross-lane traffic.
 constexpr int kMergeSmallN = 8;
-template <bool kF16>
+template <bool kF16, int kN>
 __global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerGroup + (threadIdx.x >> 6);
@@ -1005,10 +1005,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeA
   // masked below), so they issue back to back.  Each loaded vector is split
   // into scalars at once: element reads from arrays of vectors miscompile with
   // this toolchain (only element 0 survived).
-  float li[kMergeSmallN], sc[kMergeSmallN];
-  unsigned raw[kMergeSmallN][kF16 ? 4 : 8];
+  float li[kN], sc[kN];
+  unsigned raw[kN][kF16 ? 4 : 8];
 #pragma unroll
-  for (int i = 0; i < kMergeSmallN; ++i) {
+  for (int i = 0; i < kN; ++i) {
     const int64_t pr = part0 + (int64_t)min(i, a.n - 1) * a.rows;
     li[i] = a.lse_parts[pr];
     if constexpr (kF16) {
@@ -1031,13 +1031,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeA
   // partials past n, and partials with lse = -inf, get weight 0.
   float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMergeSmallN; ++i) M = fmaxf(M, i < a.n ? li[i] : -INFINITY);
+  for (int i = 0; i < kN; ++i) M = fmaxf(M, i < a.n ? li[i] : -INFINITY);
   float W = 0.f;
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMergeSmallN; ++i) {
+  for (int i = 0; i < kN; ++i) {
     const float wi = (i < a.n && li[i] != -INFINITY) ? expf(li[i] - M) : 0.f;
     W += wi;
     const float ws = wi * sc[i];
@@ -1538,10 +1538,17 @@ hipError_t launch_kv_write(const KvWriteArgs &args, hipStream_t stream) {
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream) {
   const dim3 grid((unsigned)((args.rows + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup), (unsigned)args.groups);
   if (args.d_v == 512 && args.n <= kMergeSmallN) {
-    if (args.f16)
-      hipLaunchKernelGGL((merge_small_kernel<true>), grid, dim3(kMergeThreads), 0, stream, args);
-    else
-      hipLaunchKernelGGL((merge_small_kernel<false>), grid, dim3(kMergeThreads), 0, stream, args);
+    // The kernel loads kN partials unconditionally: take the smallest kN >= n.
+    const dim3 b(kMergeThreads);
+    if (args.f16) {
+      if (args.n <= 2) hipLaunchKernelGGL((merge_small_kernel<true, 2>), grid, b, 0, stream, args);
+      else if (args.n <= 4) hipLaunchKernelGGL((merge_small_kernel<true, 4>), grid, b, 0, stream, args);
+      else hipLaunchKernelGGL((merge_small_kernel<true, 8>), grid, b, 0, stream, args);
+    } else {
+      if (args.n <= 2) hipLaunchKernelGGL((merge_small_kernel<false, 2>), grid, b, 0, stream, args);
+      else if (args.n <= 4) hipLaunchKernelGGL((merge_small_kernel<false, 4>), grid, b, 0, stream, args);
+      else hipLaunchKernelGGL((merge_small_kernel<false, 8>), grid, b, 0, stream, args);
+    }
   } else if (args.f16) {
     if (args.d_v % 128) return hipErrorInvalidValue;
     hipLaunchKernelGGL((merge_kernel<true, 8>), grid, dim3(kMergeThreads), 0, stream, args);

@@ -139,7 +139,7 @@ def test_sharded_then_merge_equals_unsharded():
     assert_lse_close(mlse, rl, "merged")
 
 
-@pytest.mark.parametrize("n,rows,d_v", [(5, 300, 512), (3, 7, 12), (70, 5, 136)])
+@pytest.mark.parametrize("n,rows,d_v", [(1, 9, 512), (2, 40, 512), (4, 33, 512), (5, 300, 512), (3, 7, 12), (70, 5, 136)])
 def test_merge_kernel_against_oracle(n, rows, d_v):
     """Public merge of fp32 partials; d_v = 12 takes the 4-column path, n = 70
     more partials than a wave has lanes, rows not a multiple of the rows per
@@ -147,7 +147,7 @@ def test_merge_kernel_against_oracle(n, rows, d_v):
     g = np.random.default_rng(3 + n)
     o = g.standard_normal((n, rows, d_v)).astype(np.float32)
     l = (g.standard_normal((n, rows)) * 4).astype(np.float32)
-    l[1, :50] = -np.inf
+    l[min(1, n - 1), :50] = -np.inf
     empty = rows // 2 + 1
     l[:, empty] = -np.inf
     ro, rl = oracle.merge(o.astype(np.float64), l.astype(np.float64))
