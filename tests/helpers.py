@@ -56,3 +56,49 @@ def workload(q_bits, logical, block_size=16, scale=1.0 / np.sqrt(192.0), seed=0,
 
 def random_rows(rng, n, cols=D_QK, std=1.0):
     return bf16(rng.standard_normal((n, cols)) * std)
+
+
+def validate_device_inputs(w: Workload) -> dict:
+    """Test-only check of the device data a decode call trusts without looking.
+
+    The library validates shapes on the host but not the contents of seq_lens,
+    block_table and indices: an attended position whose block id is outside
+    [0, num_blocks) is skipped on the device, and list entries outside
+    [0, pos(b, q)] are dropped.  This reports what a caller should have ruled
+    out: `bad_seq_lens` (outside [Q, max_blocks * block_size]), `bad_blocks`
+    ((b, logical block) pairs below S_b whose id is out of range), and for
+    sparse lists `out_of_range` (entries that are neither -1 padding nor in
+    [0, S_b - 1]: no query token can attend them), `causal_masked` (entries in
+    range but past pos(b, q), dropped for that token only: normal for a list
+    shared by the Q tokens) and `duplicates` (positions listed twice for one
+    query token).
+    """
+    num_blocks, bs = w.kv.shape[0], w.block_size
+    rep = dict(bad_seq_lens=[], bad_blocks=[], out_of_range=0, causal_masked=0, padding=0, duplicates=0)
+    for b in range(w.B):
+        S = int(w.seq_lens[b])
+        if S < w.Q or S > w.block_table.shape[1] * bs:
+            rep["bad_seq_lens"].append(b)
+            continue
+        for j in range((S + bs - 1) // bs):
+            blk = int(w.block_table[b, j])
+            if blk < 0 or blk >= num_blocks:
+                rep["bad_blocks"].append((b, j))
+        if w.indices is None:
+            continue
+        flat = np.asarray(w.indices).reshape(-1)
+        for q in range(w.Q):
+            start = b * w.index_stride_b + q * w.index_stride_q
+            lst = flat[start:start + w.top_k].astype(np.int64)
+            pos = S - w.Q + q
+            rep["padding"] += int(np.count_nonzero(lst == -1))
+            rep["out_of_range"] += int(np.count_nonzero((lst != -1) & ((lst < 0) | (lst >= S))))
+            rep["causal_masked"] += int(np.count_nonzero((lst > pos) & (lst < S)))
+            valid = lst[(lst >= 0) & (lst <= pos)]
+            rep["duplicates"] += int(valid.size - np.unique(valid).size)
+    return rep
+
+
+def device_inputs_ok(w: Workload) -> bool:
+    rep = validate_device_inputs(w)
+    return not rep["bad_seq_lens"] and not rep["bad_blocks"] and rep["out_of_range"] == 0

@@ -75,3 +75,38 @@ def test_outliers_scale_only_rope_columns():
 def test_attended_count_bookkeeping():
     w = W.make_workload("t", 2, 2, 4, [10, 3], 4, seed=1)
     assert W.attended_count(w) == (9 + 10) + (2 + 3)
+
+
+def test_generated_workloads_pass_the_device_data_validator():
+    # the workload generators at reduced sizes (the same code paths as the
+    # full-size presets: dense paging, short sparse rows, a list shared by Q = 2)
+    from helpers import validate_device_inputs
+    cases = [W.config_tiny(),
+             W.make_workload("dense", 4, 1, 16, [4096, 77, 1, 300], 64, seed=1),
+             W.make_workload("sparse", 10, 1, 16, [8192] * 10, 64, seed=2, top_k=2048, short_rows=3,
+                             short_valid=1500),
+             W.make_workload("mtp", 6, 2, 16, [1024, 1500, 3000, 5000, 2048, 4097], 64, seed=3, top_k=2048)]
+    for w in cases:
+        rep = validate_device_inputs(w)
+        assert not rep["bad_seq_lens"] and not rep["bad_blocks"], w.name
+        assert rep["out_of_range"] == 0 and rep["duplicates"] == 0, w.name
+    assert validate_device_inputs(cases[2])["padding"] == 3 * (2048 - 1500)
+    assert validate_device_inputs(cases[3])["padding"] == 2 * (2048 - 1024) + 2 * (2048 - 1500)
+
+
+def test_validator_flags_what_the_device_would_skip():
+    from helpers import validate_device_inputs
+    w = W.make_workload("bad", 3, 2, 16, [100, 300, 64], 64, seed=5, top_k=40, shared_q_indices=False)
+    w.block_table[1, 2] = w.kv.shape[0]         # block 2 of sequence 1 (positions 128..191) out of range
+    w.block_table[0, 3] = -1                     # beyond S_0 = 100 (blocks 0, 1): never attended, not flagged
+    w.seq_lens[2] = 1                            # below Q = 2
+    idx = w.indices.reshape(3, 2, 40)
+    masked0 = validate_device_inputs(w)["causal_masked"]
+    idx[0, 0, :3] = [98, -5, 1000]               # 98 = pos(0, 0); -5 and 1000 are out of range
+    idx[0, 1, 0] = idx[0, 1, 1]                  # a duplicate
+    idx[0, 1, 2] = 99                            # pos(0, 1) = 99: in range
+    idx[0, 0, 5] = 99                            # past pos(0, 0): masked for q = 0 only
+    rep = validate_device_inputs(w)
+    assert rep["bad_blocks"] == [(1, 2)] and rep["bad_seq_lens"] == [2]
+    assert rep["out_of_range"] == 2 and rep["duplicates"] >= 1
+    assert rep["causal_masked"] >= 1 and masked0 >= 0
