@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "mla_internal.h"
 
@@ -272,10 +273,17 @@ __device__ __forceinline__ TileMask tile_mask(const DecodeArgs &a, const Unit &u
 #pragma clang diagnostic ignored "-Winline-asm"
 // M0 = lds_base + lds_off (an immediate once the copy loop is unrolled), one
 // wait state for the M0 write to reach the direct load, then the load.
-__device__ __forceinline__ void dma16(const char *src, unsigned lds_base, int lds_off) {
-  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// The source offset is the instruction's immediate (a constant up to 1 KiB here,
+// within its signed 13-bit range), so a copy needs no address arithmetic.  The
+// immediate is added to the LDS address as well as to the global one, so M0 is
+// set that much lower.
+template <int kSrcOff, int kLdsOff>
+__device__ __forceinline__ void dma16(const char *src, unsigned lds_base) {
+  static_assert(kSrcOff >= 0 && kSrcOff < 4096, "immediate offset range");
+  static_assert(kLdsOff >= kSrcOff, "M0 offset stays non-negative");
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"
                :
-               : "s"(lds_base), "v"(src), "i"(lds_off)
+               : "s"(lds_base), "v"(src), "i"(kLdsOff - kSrcOff), "i"(kSrcOff)
                : "m0");
 }
 #pragma clang diagnostic pop
@@ -326,14 +334,23 @@ __device__ __forceinline__ TileCopy prepare_copy(char *tile_buf, const DecodeArg
   return copy_from_rows(tile_buf, a, wave, lane, copy_rows(tile_row, wave, lane));
 }
 
-__device__ __forceinline__ void copy_step(const TileCopy &c, int j) {
-  const int k = j / kGroups, g = j % kGroups;
-  dma16(c.src[k] + g * 128, c.lds[k], g * kGroupBytes);
+template <int kJ>
+__device__ __forceinline__ void copy_step(const TileCopy &c) {
+  constexpr int k = kJ / kGroups, g = kJ % kGroups;
+  dma16<g * 128, g * kGroupBytes>(c.src[k], c.lds[k]);
 }
-
+template <int... kJ>
+__device__ __forceinline__ void copy_steps(const TileCopy &c, std::integer_sequence<int, kJ...>) {
+  (copy_step<kJ>(c), ...);
+}
 __device__ __forceinline__ void copy_all(const TileCopy &c) {
-#pragma unroll
-  for (int j = 0; j < kCopySteps; ++j) copy_step(c, j);
+  copy_steps(c, std::make_integer_sequence<int, kCopySteps>());
+}
+// Copy step j where j is a constant once the tile loop is unrolled (the
+// comparisons then fold to the one call).
+template <int... kJ>
+__device__ __forceinline__ void copy_step_at(const TileCopy &c, int j, std::integer_sequence<int, kJ...>) {
+  ((j == kJ ? copy_step<kJ>(c) : void()), ...);
 }
 
 // acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 with (1, 1)).
@@ -606,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         if (step == 5) mask1 = tile_mask(a, u, pn1, row1);
         if (step >= kCopyFirst && (step - kCopyFirst) % kCopyEvery == 0 &&
             (step - kCopyFirst) / kCopyEvery < kCopySteps)
-          copy_step(next_copy, (step - kCopyFirst) / kCopyEvery);
+          copy_step_at(next_copy, (step - kCopyFirst) / kCopyEvery, std::make_integer_sequence<int, kCopySteps>());
       };
 
       const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
