@@ -139,7 +139,8 @@ def cpu_baseline(w, target_s: float, seed: int = 0):
 
 
 def run_kv_write(args, torch, md, W, dev):
-    """Latent KV-cache write: T = 32768 tokens per call into a 262144-slot cache
+    """Latent KV-cache write: T = 32768 prefill tokens per call (8 sequences of
+    4096, each filling 64-slot blocks drawn at random) into a 262144-slot cache
     (302 MB), cycling through 8 input sets (302 MB of new rows) so the Infinity
     Cache cannot serve them.  Bytes = each stored row read and written once
     (2 x 1152 B) + the 4-byte slot of every token."""
@@ -266,6 +267,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--topk-batch", type=int, default=32, help="rows of the top-k workload (--op topk)")
+    ap.add_argument("--group-rows", type=int, default=0, choices=[0, 64, 128],
+                    help="work-group shape (query rows per work-group); 0 = the planner's choice")
     ap.add_argument("--op", default="decode", choices=["decode", "kv_write", "topk"],
                     help="decode: the attention call (default); kv_write: the latent-cache write "
                          "through slot_mapping (32768 prefill tokens into a 262144-slot cache); "
@@ -301,6 +304,7 @@ def main():
     if args.op == "topk":
         run_topk(args, torch, md, W, dev)
         return
+    md.GROUP_ROWS = args.group_rows
     t0 = time.time()
     w = W.CONFIGS[args.config]()
     d = upload(w, dev)

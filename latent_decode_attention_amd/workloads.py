@@ -300,21 +300,43 @@ class KvWriteInputs:
 
 
 def make_kv_write_inputs(T: int, num_slots: int, seed: int, skip_frac: float = 0.1,
-                         out_of_range: int = 2) -> KvWriteInputs:
-    """T rows of N(0,1) -> bf16 bits; distinct slots drawn from [0, num_slots) (a
-    skip_frac share replaced by -1, and `out_of_range` entries set at or past the
-    end of the cache); positions 0..T-1 shuffled (a prefill's tokens)."""
-    g_rows, g_slots, g_pos = _children(seed, 3)
+                         out_of_range: int = 2, block_size: int = 64, seq_tokens: int = 4096) -> KvWriteInputs:
+    """A prefill batch's new rows and their slot map, shaped like a paged cache's:
+    the T tokens form sequences of up to `seq_tokens` tokens at positions 0, 1, ...;
+    each sequence's blocks are distinct physical blocks drawn by a seeded
+    permutation of the cache's num_slots / block_size blocks, and token p of a
+    sequence goes to slot block[p / block_size] * block_size + p mod block_size
+    (the DCP page's table A: slot_mapping into [N_blk, block_size, D]).  Rows are
+    N(0,1) -> bf16 bits.  A skip_frac share of the slots is replaced by -1 and
+    `out_of_range` entries by slots at or past the end of the cache.  Caches too
+    small for whole blocks get distinct single slots."""
+    g_rows, g_slots, _ = _children(seed, 3)
     rows = _normal_bf16(g_rows, (T, D_QK))
-    slots = g_slots.choice(num_slots, size=T, replace=False).astype(np.int32) if T <= num_slots else \
-        np.arange(T, dtype=np.int32) % num_slots
+    lens = [min(seq_tokens, T - o) for o in range(0, T, seq_tokens)]
+    bs = block_size
+    if sum((n + bs - 1) // bs for n in lens) > num_slots // bs:
+        bs = 1
+    blocks = g_slots.permutation(num_slots // bs) if num_slots >= bs else np.zeros(0, dtype=np.int64)
+    slots = np.empty(T, dtype=np.int32)
+    positions = np.empty(T, dtype=np.int32)
+    o = used = 0
+    for n in lens:
+        p = np.arange(n)
+        nb = (n + bs - 1) // bs
+        own = blocks[used:used + nb]
+        used += nb
+        if len(own) == nb:
+            slots[o:o + n] = own[p // bs] * bs + p % bs
+        else:  # more tokens than slots: wrap around the cache
+            slots[o:o + n] = (o + p) % num_slots
+        positions[o:o + n] = p
+        o += n
     if T:
         skip = g_slots.random(T) < skip_frac
         slots[skip] = -1
         k = min(out_of_range, T)
         far = g_slots.choice(T, size=k, replace=False)
         slots[far] = num_slots + np.arange(k, dtype=np.int32)
-    positions = g_pos.permutation(T).astype(np.int32)
     return KvWriteInputs(rows=rows, slots=slots, positions=positions, num_slots=num_slots)
 
 
