@@ -819,7 +819,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const u32x4 d = *reinterpret_cast<const u32x4 *>(stage + row * kStride + byte);
       const int rl = 32 * rt + row;
       if (rl < u.rows)
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(obase) + (out_row(rl) * kDv + 128 * wave) * kEsz + byte) = d;
+        __builtin_nontemporal_store(
+            d, reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(obase) + (out_row(rl) * kDv + 128 * wave) * kEsz + byte));
     }
   };
 #pragma unroll
@@ -1076,10 +1077,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeA
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
   const int64_t out_row = (int64_t)g * a.rows + r;
+  if (a.out_fp32) {
 #pragma unroll
-  for (int e = 0; e < 8; e += 4)
-    store_out(a.out, a.out_fp32 ? kOutFp32 : kOutBf16, out_row * a.d_v + c + e,
-              f32x4{s[e] * inv, s[e + 1] * inv, s[e + 2] * inv, s[e + 3] * inv});
+    for (int e = 0; e < 8; e += 4)
+      store_out(a.out, kOutFp32, out_row * a.d_v + c + e, f32x4{s[e] * inv, s[e + 1] * inv, s[e + 2] * inv, s[e + 3] * inv});
+  } else {
+    // The lane's 8 bf16 values as one 16-byte store, past the caches (the
+    // result is not read again by this call).
+    const u32x4 h = {pack_bf16(s[0] * inv, s[1] * inv), pack_bf16(s[2] * inv, s[3] * inv),
+                     pack_bf16(s[4] * inv, s[5] * inv), pack_bf16(s[6] * inv, s[7] * inv)};
+    __builtin_nontemporal_store(h, reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(a.out) + out_row * a.d_v + c));
+  }
   if (lane == 0) a.lse_out[out_row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
