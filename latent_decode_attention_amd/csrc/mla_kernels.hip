@@ -1119,8 +1119,8 @@ __global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWrite
         }
         if (store) {
           const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.rows) + t * kRowBytes);
-          v[k][0] = src[lane];
-          if (lane < kChunks - 64) v[k][1] = src[64 + lane];
+          v[k][0] = __builtin_nontemporal_load(src + lane);
+          if (lane < kChunks - 64) v[k][1] = __builtin_nontemporal_load(src + 64 + lane);
           dst_row[k] = slot;
         }
       }
@@ -1129,8 +1129,8 @@ __global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWrite
     for (int k = 0; k < kKvRowsPerWave; ++k) {
       if (dst_row[k] < 0) continue;  // the whole wave takes the same branch
       u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.kv) + dst_row[k] * kRowBytes);
-      dst[lane] = v[k][0];
-      if (lane < kChunks - 64) dst[64 + lane] = v[k][1];
+      __builtin_nontemporal_store(v[k][0], dst + lane);
+      if (lane < kChunks - 64) __builtin_nontemporal_store(v[k][1], dst + 64 + lane);
     }
   }
 }
