@@ -1031,13 +1031,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_small_kernel(const MergeA
     li[i] = a.lse_parts[pr];
     if constexpr (kF16) {
       sc[i] = a.scale_parts[pr * 4 + (c >> 7)];
-      const u32x4 h = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const _Float16 *>(a.o_parts) + pr * 512 + c);
+      const u32x4 h = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(reinterpret_cast<const _Float16 *>(a.o_parts) + pr * 512 + c));
 #pragma unroll
       for (int e = 0; e < 4; ++e) raw[i][e] = h[e];
     } else {
       sc[i] = 1.f;
       const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.o_parts) + pr * 512 + c);
-      const u32x4 lo = src[0], hi = src[1];
+      const u32x4 lo = __builtin_nontemporal_load(src), hi = __builtin_nontemporal_load(src + 1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         raw[i][e] = lo[e];
