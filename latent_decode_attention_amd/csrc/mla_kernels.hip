@@ -173,24 +173,36 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 
 template <int kMode>
 __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
-  const int64_t grid = (int64_t)gridDim.x;
-  int64_t id = blockIdx.x;
+  const uint32_t grid = gridDim.x;  // < 2^31 (the plan checks)
+  uint32_t id = blockIdx.x;
   // Work-groups are dealt round-robin to the 8 XCDs; renumber so that the
   // partitions of one unit (which share the unit's query rows) sit on one XCD.
   if ((grid & 7) == 0) id = (id & 7) * (grid >> 3) + (id >> 3);
+  // 32-bit unsigned arithmetic: the 64-bit divisions this replaced were a long
+  // branchy sequence in front of the first loads.
   Unit u;
-  u.split = (int)(id % a.splits);
-  id /= a.splits;
-  const int qg = (int)(id % a.q_groups);
-  id /= a.q_groups;
-  const int su = (int)(id % a.shard_units);
-  u.b = (int)(id / a.shard_units);
-  u.q0 = (qg / a.head_chunks) * a.q_per_group;
-  u.h0 = (qg % a.head_chunks) * a.rows_per_group;
+  const uint32_t splits = a.splits, q_groups = a.q_groups, shard_units = a.shard_units, head_chunks = a.head_chunks;
+  u.split = (int)(id % splits);
+  id /= splits;
+  const uint32_t qg = id % q_groups;
+  id /= q_groups;
+  const int su = (int)(id % shard_units);
+  u.b = (int)(id / shard_units);
+  u.q0 = (int)(qg / head_chunks) * a.q_per_group;
+  u.h0 = (int)(qg % head_chunks) * a.rows_per_group;
   u.rows = min(a.rows_per_group, a.q_per_group * a.h_q - u.h0);
   u.row0 = uniform(((int64_t)u.b * a.Q + u.q0) * a.h_q + u.h0);
   u.shard = a.shard_base + su;
-  u.S = uniform(a.seq_lens[u.b]);
+  if constexpr (kMode == kSparseStream) {
+    // Only the causal checks, after the first index and block loads, use the
+    // length: read it with a vector load and leave it in a register, so that
+    // no wait on scalar loads in front of those loads covers it.
+    int bl = u.b;
+    asm volatile("" : "+v"(bl));
+    u.S = a.seq_lens[bl];
+  } else {
+    u.S = uniform(a.seq_lens[u.b]);
+  }
   int L;
   u.idx_base = 0;
   bool rest = false;  // the last partition also takes what the plan did not foresee
