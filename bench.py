@@ -44,7 +44,7 @@ def kernel_hash() -> str:
 
 
 def algorithmic_work(w, indices_list=None):
-    """Bytes and flops the method must move/compute for one step (see DESIGN.md).
+    """Bytes and flops the method must move/compute for one step.
 
     bytes = latent rows attended (each once per sequence) x 1152 + q + O + lse
             + index lists + block-table entries of the blocks touched
