@@ -115,6 +115,34 @@ def test_sparse_out_of_range_duplicates_and_causal_limit():
     check_full(w, torch.float32)
 
 
+EDGE_SHAPES = {
+    # name: (B, Q, h_q, seq_lens, block_size, top_k, shared list)
+    "one_head": (2, 1, 1, [300, 65], 16, 0, True),
+    "three_heads_two_tokens": (2, 2, 3, [129, 64], 16, 0, True),
+    "heads_96_dense": (2, 2, 96, [700, 1500], 64, 0, True),
+    "heads_96_sparse_per_token": (2, 2, 96, [700, 1500], 64, 300, False),
+    "sixteen_tokens_8_heads": (2, 16, 8, [200, 1000], 16, 0, True),
+    "four_tokens_shared_list": (3, 4, 16, [100, 2000, 4096], 64, 512, True),
+    "one_token_pages": (2, 1, 16, [100, 37], 1, 0, True),
+    "largest_pages": (2, 1, 32, [5000, 300], 4096, 0, True),
+    "largest_list": (1, 1, 16, [70000], 64, 65536, True),
+    "six_hundred_sequences": (600, 1, 16, [int(x) for x in np.random.default_rng(5).integers(1, 200, 600)], 16, 0,
+                              True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_SHAPES))
+def test_edge_shapes(name):
+    """Limits of the supported range: 1, 3 and 96 heads (a 64- and a 32-head
+    chunk), 16 query tokens, 1- and 4096-token pages, a 65536-entry list (one
+    unit cut into many partitions, merged by the general merge kernel) and 600
+    sequences (more units than CUs)."""
+    B, Q, h, lens, bs, k, shared = EDGE_SHAPES[name]
+    w = W.make_workload(name, B, Q, h, lens, bs, seed=sum(map(ord, name)), top_k=k, shared_q_indices=shared,
+                        spare_blocks=2)
+    check_full(w, torch.float32)
+
+
 def test_sharded_then_merge_equals_unsharded():
     w = W.make_workload("sharded", 2, 1, 128, [3000, 1111], 16, seed=51, num_shards=3, interleave=16)
     d = upload(w)
