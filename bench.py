@@ -267,6 +267,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--topk-batch", type=int, default=32, help="rows of the top-k workload (--op topk)")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="list length for a sparse preset (0 = the preset's own; a per-tile cost is the "
+                         "difference of two lengths)")
     ap.add_argument("--group-rows", type=int, default=0, choices=[0, 64, 128],
                     help="work-group shape (query rows per work-group); 0 = the planner's choice")
     ap.add_argument("--op", default="decode", choices=["decode", "kv_write", "topk"],
@@ -306,7 +309,14 @@ def main():
         return
     md.GROUP_ROWS = args.group_rows
     t0 = time.time()
-    w = W.CONFIGS[args.config]()
+    if args.top_k:
+        w = W.CONFIGS[args.config]()
+        if w.indices is None or w.index_stride_q != 0:
+            raise SystemExit("--top-k applies to the sparse presets with one list per sequence")
+        w = W.make_workload(f"{w.name}_k{args.top_k}", w.B, w.Q, w.h_q, w.seq_lens, w.block_size,
+                            int(w.meta["seed"]), top_k=args.top_k)
+    else:
+        w = W.CONFIGS[args.config]()
     d = upload(w, dev)
     print(f"[bench] workload {w.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
