@@ -46,7 +46,8 @@ def kernel_hash() -> str:
 def algorithmic_work(w, indices_list=None):
     """Bytes and flops the method must move/compute for one step.
 
-    bytes = latent rows attended (each once per sequence) x 1152 + q + O + lse
+    bytes = latent rows attended (each once per sequence) x 1152 (int8 cache: 576 + a
+            4-byte row factor) + q + O + lse
             + index lists + block-table entries of the blocks touched
             (+ the fp32 shard partials written and read, under DCP).
     flops = sum_{b,q} |A(b,q)| * h_q * 2 * (576 + 512).
@@ -66,7 +67,7 @@ def algorithmic_work(w, indices_list=None):
             lst = np.asarray(lst)
             need = set(int(i) for i in lst if 0 <= i <= S - 1)
             per_q = [int(np.count_nonzero((lst >= 0) & (lst <= S - Q + qi))) for qi in range(Q)]
-        rows_bytes += len(need) * 1152
+        rows_bytes += len(need) * (1152 if w.kv8 is None else 576 + 4)
         bt_bytes += len({p // w.block_size for p in need}) * 4
         kv_heads += sum(per_q) * H
     q_bytes = B * Q * H * 576 * 2
@@ -270,6 +271,8 @@ def main():
     ap.add_argument("--top-k", type=int, default=0,
                     help="list length for a sparse preset (0 = the preset's own; a per-tile cost is the "
                          "difference of two lengths)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
+                    help="latent cache element type: bf16, or int8 codes with one fp32 factor per row")
     ap.add_argument("--group-rows", type=int, default=0, choices=[0, 64, 128],
                     help="work-group shape (query rows per work-group); 0 = the planner's choice")
     ap.add_argument("--op", default="decode", choices=["decode", "kv_write", "topk"],
@@ -317,6 +320,8 @@ def main():
                             int(w.meta["seed"]), top_k=args.top_k)
     else:
         w = W.CONFIGS[args.config]()
+    if args.kv == "int8":
+        w = W.int8_cache(w)
     d = upload(w, dev)
     print(f"[bench] workload {w.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
@@ -329,10 +334,10 @@ def main():
         kv_dev = [d.kv]
     else:
         idx_host, idx_dev = None, None
-        copies = max(1, min(args.rotate, int((2 << 30) // max(1, d.kv.numel() * 2))))
+        copies = max(1, min(args.rotate, int((2 << 30) // max(1, d.kv.numel() * d.kv.element_size()))))
         kv_dev = [d.kv] + [d.kv.clone() for _ in range(copies - 1)]
 
-    p0 = md.make_problem(d.q, d.kv, d.block_table, d.seq_lens, w.scale, w.max_seq_len)
+    p0 = md.make_problem(d.q, d.kv, d.block_table, d.seq_lens, w.scale, w.max_seq_len, d.kv_scale)
     plan = md.mla_plan_query(p0, num_shards=w.num_shards, interleave=w.interleave,
                              top_k=w.top_k, index_stride_q=w.index_stride_q,
                              num_cus=torch.cuda.get_device_properties(dev).multi_processor_count)
@@ -356,11 +361,12 @@ def main():
                                  max_seq_len=w.max_seq_len, top_k=w.top_k, index_stride_b=w.index_stride_b,
                                  index_stride_q=w.index_stride_q, num_shards=w.num_shards,
                                  interleave=w.interleave, shard_id=-1, out=out, lse=lse,
-                                 workspace=workspace, stream=stream)
+                                 workspace=workspace, stream=stream, kv_scale=d.kv_scale)
         else:
             md.mla_decode_dense(d.q, kv_dev[r], d.block_table, d.seq_lens, scale=w.scale,
                                 max_seq_len=w.max_seq_len, num_shards=w.num_shards, interleave=w.interleave,
-                                shard_id=-1, out=out, lse=lse, workspace=workspace, stream=stream)
+                                shard_id=-1, out=out, lse=lse, workspace=workspace, stream=stream,
+                                kv_scale=d.kv_scale)
         if sharded:
             md.mla_merge_lse(out, lse, out=merged, lse_out=mlse, stream=stream)
 
@@ -411,7 +417,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Q": w.Q, "h_q": w.h_q,
+        "config": {"workload": w.name, "B": w.B, "Q": w.Q, "h_q": w.h_q, "kv_dtype": args.kv,
                    "seq_len": int(w.max_seq_len), "top_k": w.top_k or None,
                    "num_shards": w.num_shards, "block_size": w.block_size,
                    "out_dtype": args.out_dtype, "rotating_input_sets": len(idx_dev or kv_dev),

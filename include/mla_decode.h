@@ -70,7 +70,7 @@ typedef struct {
   float scale;                /* softmax scale applied to <q, k>: finite and > 0 */
   const void *q;              /* device, bf16 [B, Q, h_q, d_qk] (query already absorbed
                                  into the latent space; RoPE part last) */
-  const void *kv;             /* device, bf16 [num_blocks, block_size, d_qk] */
+  const void *kv;             /* device, [num_blocks, block_size, d_qk] in kv_dtype */
   int32_t num_blocks;         /* >= 1 */
   int32_t block_size;         /* tokens per block, a power of two, 1..4096 */
   const int32_t *block_table; /* device, int32 [B, max_blocks] physical block ids */
@@ -84,7 +84,23 @@ typedef struct {
                                  64-row groups need no KV partitions while 128-row groups
                                  would, or when 128-row partitions would be 4 tiles or
                                  fewer.  Any other value: MLA_ERR_BAD_SHAPE */
+  /*
+   * Element type of the latent cache (the int8 cache is the one-byte "kv-int8"
+   * element type of "RFC: MsModeling 支持 Decode Context Parallel", the notation
+   * table of §2.1.4, listed again among the open items of §3.3; the pages state
+   * no dequantisation rule).  MLA_KV_BF16 (0, the default of a zeroed struct): `kv` holds bf16 and
+   * `kv_scale` is ignored.  MLA_KV_INT8 (1): `kv` holds int8 and `kv_scale`
+   * one fp32 factor per cache row, device fp32 [num_blocks, block_size]; the
+   * row's value is kv_scale[row] * kv[row, c] for all 576 columns (keys and the
+   * value columns alike).  Int8 caches run with 64-row work-groups only
+   * (group_rows 128 with MLA_KV_INT8: MLA_ERR_UNSUPPORTED).  A null kv_scale
+   * with MLA_KV_INT8: MLA_ERR_NULL_POINTER; another kv_dtype: MLA_ERR_UNSUPPORTED.
+   */
+  int32_t kv_dtype;
+  const float *kv_scale;
 } mla_problem_t;
+
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_INT8 = 1 } mla_kv_dtype_t;
 
 /*
  * Bytes of scratch the decode call needs for its split-KV partial results

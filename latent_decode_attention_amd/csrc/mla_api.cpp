@@ -62,6 +62,12 @@ mla_status_t check_problem(const mla_problem_t *p) {
   if (p->group_rows != 0 && p->group_rows != 64 && p->group_rows != 128) return MLA_ERR_BAD_SHAPE;
   if ((reinterpret_cast<uintptr_t>(p->q) | reinterpret_cast<uintptr_t>(p->kv)) & 15)
     return MLA_ERR_BAD_SHAPE;  // rows are moved in 16-byte pieces
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_INT8) return MLA_ERR_UNSUPPORTED;
+  if (p->kv_dtype == MLA_KV_INT8) {
+    if (!p->kv_scale) return MLA_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(p->kv_scale) & 3) return MLA_ERR_BAD_SHAPE;
+    if (p->group_rows == 128) return MLA_ERR_UNSUPPORTED;  // int8 tiles leave no LDS for 128 rows
+  }
   return MLA_OK;
 }
 
@@ -157,8 +163,9 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   const int64_t wide_tiles = wide.chunk / kTile;
   const int forced = p->group_rows;
   const bool use_narrow =
-      forced ? forced == 64
-             : wide.rows_per_group <= 64 || (narrow.splits == 1 && wide.splits > 1) || wide_tiles <= 4;
+      p->kv_dtype == MLA_KV_INT8 ||
+      (forced ? forced == 64
+              : wide.rows_per_group <= 64 || (narrow.splits == 1 && wide.splits > 1) || wide_tiles <= 4);
   *pl = use_narrow ? narrow : wide;
   const int64_t splits = pl->splits;
   const int64_t rows_total = (int64_t)p->B * p->Q * p->h_q;
@@ -206,6 +213,8 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
   std::memset(&a, 0, sizeof a);
   a.q = static_cast<const uint16_t *>(p->q);
   a.kv = static_cast<const uint16_t *>(p->kv);
+  a.kv8 = p->kv_dtype == MLA_KV_INT8 ? 1 : 0;
+  a.kv_scale = a.kv8 ? p->kv_scale : nullptr;
   a.block_table = p->block_table;
   a.seq_lens = p->seq_lens;
   a.indices = indices;

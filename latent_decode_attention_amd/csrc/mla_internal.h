@@ -21,7 +21,7 @@ constexpr int kMaxQPerGroup = 4;       // query tokens per work-group (attended 
 // Everything one decode launch needs.  Passed by value as the kernel argument.
 struct DecodeArgs {
   const uint16_t *q;           // bf16 [B, Q, h_q, 576]
-  const uint16_t *kv;          // bf16 [num_blocks, block_size, 576]
+  const uint16_t *kv;          // bf16 [num_blocks, block_size, 576], or int8 when kv8
   const int32_t *block_table;  // [B, max_blocks]
   const int32_t *seq_lens;     // [B]
   const int32_t *indices;      // sparse only
@@ -53,6 +53,9 @@ struct DecodeArgs {
   float *part_lse;
   float *part_scale;
   int32_t part_f16;
+  // int8 cache (kv8): `kv` holds int8 rows and kv_scale fp32 [num_blocks, block_size] their factors
+  int32_t kv8;
+  const float *kv_scale;
 };
 
 struct MergeArgs {

@@ -61,6 +61,14 @@ constexpr int kQkSteps = kDqk / 16;            // 36 k-steps of the 32x32x16 MFM
 constexpr int kGroups = kChunks / 8;           // 9 column groups of 128 bytes
 constexpr int kGroupBytes = kTile * 128;       // 8192
 constexpr int kCopySteps = 2 * kGroups;        // direct-load instructions per wave per tile
+// int8 cache: a row is 576 bytes; a tile's raw rows fill half a bf16 tile buffer.
+constexpr int kRowBytes8 = kDqk;                      // 576
+constexpr int kRawTileBytes = kTile * kRowBytes8;     // 36864
+constexpr int kCopySteps8 = 16 * kRowBytes8 / 1024;   // 9 direct loads of 1 KiB per wave per tile
+static_assert(2 * kRawTileBytes == kTileBytes, "two raw int8 tiles share one bf16 tile buffer");
+// Bias of the widened int8 values: byte b is held as b + 128 in [0, 255], an
+// integer bf16 represents exactly.
+constexpr float kKv8Bias = 128.0f;
 // How far (base 2) a score may exceed its row's reference maximum before the
 // unit is recomputed with a higher reference: p <= 2^60 keeps sum(p) * |v| far
 // inside the fp32 range for any realistic row.
@@ -86,6 +94,8 @@ struct __attribute__((aligned(16))) Smem<64> {
   char tile[2][kTileBytes];
   bf16x8 p[4][2][64];
   float mx[kWaves][32];  // first-tile row maxima exchanged by the two waves of a row tile
+  float sig[kTile];      // int8 cache: the current tile's row factors (tiny for unattended tokens)
+  float sig_inv[kTile];  // ... and their inverses
 };
 static_assert(sizeof(Smem<128>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024, "LDS budget of one work-group");
 
@@ -365,6 +375,39 @@ __device__ __forceinline__ void copy_step_at(const TileCopy &c, int j, std::inte
   ((j == kJ ? copy_step<kJ>(c) : void()), ...);
 }
 
+// Copy of one int8 tile into a raw buffer: wave w copies rows 16w..16w+15 into
+// its 9 KiB slice; step j moves bytes 64 j .. 64 j + 63 of each of the 16 rows,
+// lane l taking row 16 w + l / 4 and its bytes 64 j + 16 (l % 4), which land at
+// 1024 j + 16 l.  Raw 16-byte chunk C of wave row rho therefore sits at
+// 1024 (C / 4) + 64 rho + 16 (C % 4) of the slice.
+struct TileCopy8 {
+  const char *src;  // this lane's row + 16 (l % 4); the step's 64 j is the immediate
+  unsigned lds;     // wave-uniform LDS address of the wave's slice
+};
+__device__ __forceinline__ TileCopy8 prepare_copy8(char *raw_buf, const DecodeArgs &a, int wave, int lane,
+                                                   int tile_row) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const int row = __shfl(tile_row, 16 * wave + (l >> 2));
+  const char *row_src = reinterpret_cast<const char *>(a.kv) + (int64_t)max(row, 0) * kRowBytes8;
+  TileCopy8 c;
+  c.src = (row < 0 ? reinterpret_cast<const char *>(kZeroRow) : row_src) + 16 * (l & 3);
+  c.lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(raw_buf + wave * 16 * kRowBytes8));
+  return c;
+}
+template <int kJ>
+__device__ __forceinline__ void copy_step8(const TileCopy8 &c) {
+  dma16<64 * kJ, 1024 * kJ>(c.src, c.lds);
+}
+template <int... kJ>
+__device__ __forceinline__ void copy_all8(const TileCopy8 &c, std::integer_sequence<int, kJ...>) {
+  (copy_step8<kJ>(c), ...);
+}
+template <int... kJ>
+__device__ __forceinline__ void copy_step8_at(const TileCopy8 &c, int j, std::integer_sequence<int, kJ...>) {
+  ((j == kJ ? copy_step8<kJ>(c) : void()), ...);
+}
+
 // acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 with (1, 1)).
 // Written as asm: the compiler's own lowering of the dot2 builtin misplaced its
 // operands in this kernel.
@@ -404,6 +447,32 @@ __device__ __forceinline__ void store_out(void *out, int kind, int64_t elem, f32
   }
 }
 
+// Widen the wave's 16 rows of a raw int8 tile into the bf16 tile layout.  Byte
+// b becomes b + 128 (XOR 0x80 reads the signed byte as that unsigned value),
+// exact in bf16; the kernel takes the bias back out of the scores and outputs.
+// Pass (h, g) covers 8 rows x the 8 chunks of column group g: lane l reads 8 raw
+// bytes (512 contiguous bytes per wave) and writes one 16-byte chunk (each 16
+// lanes write two whole 128-byte rows: every bank once).
+__device__ __forceinline__ void widen_tile8(const char *raw_buf, char *tile_buf, int wave, int lane) {
+  const char LDS_AS *src = (const char LDS_AS *)(raw_buf + wave * 16 * kRowBytes8 + 8 * lane);
+  const int c = lane & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = 8 * h + (lane >> 3);  // row within the wave's 16; its key is that of 16 wave + rr
+    char LDS_AS *dst = (char LDS_AS *)(tile_buf + (16 * wave + rr) * 128 + 16 * (c ^ chunk_key(rr)));
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const u32x2 w = *(const u32x2 LDS_AS *)(src + g * 1024 + h * 512);
+      const unsigned lo = w[0] ^ 0x80808080u, hi = w[1] ^ 0x80808080u;
+      const u32x4 o = {pack_bf16((float)(lo & 255u), (float)((lo >> 8) & 255u)),
+                       pack_bf16((float)((lo >> 16) & 255u), (float)(lo >> 24)),
+                       pack_bf16((float)(hi & 255u), (float)((hi >> 8) & 255u)),
+                       pack_bf16((float)((hi >> 16) & 255u), (float)(hi >> 24))};
+      *(u32x4 LDS_AS *)(dst + g * kGroupBytes) = o;
+    }
+  }
+}
+
 // Power-of-two scale for storing values of magnitude up to `vmax` as fp16: the
 // largest lands in [2^14, 2^15), so every value keeps fp16's 11-bit precision
 // down to 2^-28 of the maximum.  Returns the scale; *inv gets its exact inverse.
@@ -419,15 +488,25 @@ __device__ __forceinline__ float fp16_scale(float vmax, float *inv) {
 // kRows = 64: wave w scores row tile w & 1 against token half w >> 1 only, so
 // the two waves of a row tile (w, w ^ 2) agree on the rows' reference maximum
 // at the first tile and combine their sums at the end.
-template <int kMode, int kRows>
+//
+// kKv8 (int8 cache, 64 rows only): the raw rows of tiles t and t+1 are
+// double-buffered in the first tile buffer; at the top of tile t each wave
+// widens its own 16 rows into the second buffer, which the scores and P.V read
+// as with a bf16 cache.  Scores are sigma_p (s'_p - 128 sum(q)) with s' the
+// product against the biased values; the weights fed to P.V carry sigma_p, and
+// the outputs drop 128 x (sum of those weights) before normalising by the sum
+// of the weights over their factors.
+template <int kMode, int kRows, bool kKv8 = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
+  static_assert(!kKv8 || kRows == 64, "int8 tiles leave LDS for 64-row work-groups only");
   constexpr int kRowTiles = kRows / 32;
   constexpr int kAccTiles = 4 * kRowTiles;  // row tiles x 4 column tiles of 32 x 32
   constexpr int kSubBlocks = kRows / 64;    // 32-token score blocks per wave per tile
   constexpr int kPvSteps = 16;               // (k-block, column tile) steps of P.V
   constexpr int kCopyFirst = 3;              // first step that copies (after its addresses are formed)
-  constexpr int kCopyEvery = (kSubBlocks * kQkSteps + kPvSteps - kCopyFirst) / kCopySteps;
-  static_assert(kCopyFirst + kCopyEvery * (kCopySteps - 1) < kSubBlocks * kQkSteps + kPvSteps,
+  constexpr int kSteps = kKv8 ? kCopySteps8 : kCopySteps;  // copy instructions per wave per tile
+  constexpr int kCopyEvery = (kSubBlocks * kQkSteps + kPvSteps - kCopyFirst) / kSteps;
+  static_assert(kCopyFirst + kCopyEvery * (kSteps - 1) < kSubBlocks * kQkSteps + kPvSteps,
                 "the copy of the next tile is issued within the tile");
   __shared__ Smem<kRows> sm;
   const int tid = threadIdx.x;
@@ -496,6 +575,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // the chain leaves the query loads issued after it in flight.
   TileMask mask_cur;
   int pn1, bn1, pn2;
+  // int8 cache: the row factor each lane (= token) loaded for the current tile,
+  // and whether its token is attended at all (else the factor is taken as 0).
+  float sig_raw = 0.f;
+  bool sig_ok = false;
   auto start_pass = [&](auto between, auto after_blocks) {
     int plane = lane;
     asm volatile("" : "+v"(plane));
@@ -511,7 +594,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     after_blocks();
     __builtin_amdgcn_sched_barrier(0);
     const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
-    copy_all(prepare_copy(sm.tile[0], a, wave, lane, row0));
+    if constexpr (kKv8) {
+      copy_all8(prepare_copy8(sm.tile[0], a, wave, lane, row0), std::make_integer_sequence<int, kCopySteps8>());
+      sig_raw = a.kv_scale[max(row0, 0)];
+      sig_ok = row0 >= 0;
+    } else {
+      copy_all(prepare_copy(sm.tile[0], a, wave, lane, row0));
+    }
     mask_cur = tile_mask(a, u, p0, row0);
   };
 
@@ -579,6 +668,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const bf16x8 zero8 = {};
   unsigned ones2 = 0x3F803F80u;  // (1.0, 1.0) in bf16, kept in a register
   asm volatile("" : "+v"(ones2));
+  // int8 cache: 128 x (sum of the row's query elements), the part of each score
+  // that the bias of the widened values adds.
+  float q_bias = 0.f;
+  if constexpr (kKv8) {
+#pragma unroll
+    for (int st = 0; st < kQkSteps; ++st) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qr[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q_bias = sum_bf16_pair(q_bias, w[e], ones2);
+    }
+    q_bias = (q_bias + __shfl_xor(q_bias, 32)) * kKv8Bias;
+  }
 
   // Softmax bookkeeping for this wave's 32 rows, base-2 units.  m_ref is the
   // row's reference maximum, raised only by a recompute pass (to the largest
@@ -593,6 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   float m_seen = -INFINITY;  // largest score seen so far
   float l_run = 0.f;         // this lane's share of sum(p), for lse
   float l_rnd = 0.f;         // the same sum over p as rounded to bf16, for O
+  float l_cvx = 0.f;         // int8 cache: sum of the rounded weights over their row factors, for O
   f32x16 acc[kAccTiles];     // acc[4 rt + ct]: rows 32 rt.., columns 128 wave + 32 ct..
   bool first_pass = true;
 
@@ -603,12 +705,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     for (int i = 0; i < kAccTiles; ++i) acc_zero(acc[i], z);
     l_run = 0.f;
     l_rnd = 0.f;
+    l_cvx = 0.f;
     bool overflow = false;
 
     for (int t = 0; t < ntiles; ++t) {
       const int cur = t & 1;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t have landed
       __syncthreads();                       // ... every wave's; tile t-1's P and V are consumed
+      if constexpr (kKv8) {
+        if (wave == 0) {
+          // A zero factor (and an unattended token) is replaced by 2^-100 so
+          // that its inverse is finite: the token's weight still counts in the
+          // normaliser while its values contribute nothing measurable.
+          const float f = sig_ok && sig_raw != 0.f ? sig_raw : 0x1p-100f;
+          sm.sig[lane] = f;
+          sm.sig_inv[lane] = 1.f / f;
+        }
+        widen_tile8(sm.tile[0] + cur * kRawTileBytes, sm.tile[1], wave, lane);
+        lds_barrier();  // the widened tile and its factors are in LDS
+      }
       // Tile t+1's rows and masks (from lookups that landed with the wait
       // above), its copy addresses, and the raw lookups two and three tiles
       // ahead are worked out during the first score steps, in the MFMAs'
@@ -619,26 +734,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // last tile every row is -1 and the copy moves zero rows into the idle
       // buffer (drained after the loop), which avoids a branch per copy.
       int row1 = -1, bn2 = 0, pn3 = 0;
+      float sig1_raw = 0.f;
+      bool sig1_ok = false;
       TileMask mask1;
       CopyRows crow;
       TileCopy next_copy;
+      TileCopy8 next_copy8;
       auto tile_step_work = [&](int step) {
         if (step == 0) {
           row1 = token_row(a, u, u.i0 + (t + 1) * kTile + lane, pn1, bn1);
-          crow = copy_rows(row1, wave, lane);
+          if constexpr (kKv8) {
+            sig1_raw = a.kv_scale[max(row1, 0)];
+            sig1_ok = row1 >= 0;
+          } else {
+            crow = copy_rows(row1, wave, lane);
+          }
         }
-        if (step == 2) next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);
+        if (step == 2) {
+          if constexpr (kKv8)
+            next_copy8 = prepare_copy8(sm.tile[0] + (cur ^ 1) * kRawTileBytes, a, wave, lane, row1);
+          else
+            next_copy = copy_from_rows(sm.tile[cur ^ 1], a, wave, lane, crow);
+        }
         if (step == 4) {
           bn2 = raw_block(a, u, pn2);
           pn3 = raw_position<kMode>(a, u, u.i0 + (t + 3) * kTile + lane);
         }
         if (step == 5) mask1 = tile_mask(a, u, pn1, row1);
         if (step >= kCopyFirst && (step - kCopyFirst) % kCopyEvery == 0 &&
-            (step - kCopyFirst) / kCopyEvery < kCopySteps)
-          copy_step_at(next_copy, (step - kCopyFirst) / kCopyEvery, std::make_integer_sequence<int, kCopySteps>());
+            (step - kCopyFirst) / kCopyEvery < kSteps) {
+          if constexpr (kKv8)
+            copy_step8_at(next_copy8, (step - kCopyFirst) / kCopyEvery, std::make_integer_sequence<int, kCopySteps8>());
+          else
+            copy_step_at(next_copy, (step - kCopyFirst) / kCopyEvery, std::make_integer_sequence<int, kCopySteps>());
+        }
       };
 
-      const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[cur]);
+      const char LDS_AS *tb = (const char LDS_AS *)(sm.tile[kKv8 ? 1 : cur]);
 
 #pragma unroll
       for (int sb = 0; sb < kSubBlocks; ++sb) {
@@ -673,6 +805,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         // 32 tok + 8 (r / 4) + 4 half + r % 4 of the tile.  Scores stay unscaled
         // until the exponent (the scale is positive, so the maximum commutes).
         float x[16];
+        float sg[16], sgi[16];  // int8 cache: row factors of the lane's 16 tokens, and inverses
+        if constexpr (kKv8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&sm.sig[32 * tok + 8 * i + 4 * half]);
+            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&sm.sig_inv[32 * tok + 8 * i + 4 * half]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              sg[4 * i + j] = v4[j];
+              sgi[4 * i + j] = w4[j];
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = sg[r] * (s[r] - q_bias);
+        }
         if (mask_cur.full) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] = s[r];
@@ -711,6 +858,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int e = 0; e < 8; ++e) {
             pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * k + e], a.scale_log2, -m_use));
             l_run += pv[e];
+            if constexpr (kKv8) pv[e] *= sg[8 * k + e];  // P.V weights carry the row factors
           }
           const u32x4 w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
                            pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
@@ -718,6 +866,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           // used, so it stays an exact convex combination of the V rows.
 #pragma unroll
           for (int e = 0; e < 4; ++e) l_rnd = sum_bf16_pair(l_rnd, w[e], ones2);
+          if constexpr (kKv8) {
+            // The weights as used, divided by their factors: the softmax weights
+            // the P.V product applies to the dequantised rows.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              l_cvx = __builtin_fmaf(__builtin_bit_cast(float, w[e] << 16), sgi[8 * k + 2 * e], l_cvx);
+              l_cvx = __builtin_fmaf(__builtin_bit_cast(float, w[e] & 0xFFFF0000u), sgi[8 * k + 2 * e + 1], l_cvx);
+            }
+          }
           // P^T operand of k-block 2 tok + k, row tile rh: lane (row n, half)
           // holds tokens 16 (2 tok + k) + 8 (e / 4) + 4 half + e % 4.
           sm.p[2 * tok + k][rh][lane] = __builtin_bit_cast(bf16x8, w);
@@ -764,6 +921,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       }
 
       mask_cur = mask1;
+      sig_raw = sig1_raw;
+      sig_ok = sig1_ok;
       pn1 = pn2;
       bn1 = bn2;
       pn2 = pn3;
@@ -796,9 +955,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   float *l_sh = reinterpret_cast<float *>(sm.tile[0]);  // [sum kind][wave][32]
   const float l_run_w = l_run + __shfl_xor(l_run, 32);
   const float l_rnd_w = l_rnd + __shfl_xor(l_rnd, 32);
+  const float l_cvx_w = kKv8 ? l_cvx + __shfl_xor(l_cvx, 32) : 0.f;
   if (half == 0) {
     l_sh[wave * 32 + n] = l_run_w;
     l_sh[kWaves * 32 + wave * 32 + n] = l_rnd_w;
+    if constexpr (kKv8) l_sh[2 * kWaves * 32 + wave * 32 + n] = l_cvx_w;
   }
   lds_barrier();
   // Row sum of kind k (0: exact, 1: rounded) of row 32 r_t + n.
@@ -838,7 +999,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
     const int r = 32 * rt + n;
-    const float l = row_sum(1, rt);
+    // bf16 cache: normalised by the sum of the rounded weights used.  int8
+    // cache: the bias times that sum comes off, then division by the sum of
+    // those weights over their factors (an exact convex combination again).
+    const float l = row_sum(kKv8 ? 2 : 1, rt);
+    const float c0 = kKv8 ? kKv8Bias * row_sum(1, rt) : 0.f;
+    auto unbias = [&](float x) { return kKv8 ? x - c0 : x; };
     const bool ok = r < u.rows;
     const int64_t gr = ok ? out_row(r) : 0;
     f32x16 v[4];
@@ -852,7 +1018,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[ct][e]));
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(unbias(v[ct][e])));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       float inv_scale;
       mult *= fp16_scale(mx * mult, &inv_scale);
@@ -864,8 +1030,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 o = {v[ct][4 * i] * mult, v[ct][4 * i + 1] * mult, v[ct][4 * i + 2] * mult,
-                         v[ct][4 * i + 3] * mult};
+        const f32x4 o = {unbias(v[ct][4 * i]) * mult, unbias(v[ct][4 * i + 1]) * mult,
+                         unbias(v[ct][4 * i + 2]) * mult, unbias(v[ct][4 * i + 3]) * mult};
         const int col = 32 * ct + 8 * i + 4 * half;
         if (wide_out) {
           *reinterpret_cast<f32x4 *>(stage + n * pitch + col * 4) = o;
@@ -1538,7 +1704,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(kThreads);
   const bool wide = args.kernel_rows == 128;
-  if (args.sparse) {
+  if (args.kv8) {
+    if (wide) return hipErrorInvalidValue;  // the planner never picks 128 rows for int8
+    if (args.sparse) hipLaunchKernelGGL((decode_kernel<kSparseStream, 64, true>), g, b, 0, stream, args);
+    else if (args.num_shards > 1) hipLaunchKernelGGL((decode_kernel<kShardStream, 64, true>), g, b, 0, stream, args);
+    else hipLaunchKernelGGL((decode_kernel<kDenseStream, 64, true>), g, b, 0, stream, args);
+  } else if (args.sparse) {
     if (wide) hipLaunchKernelGGL((decode_kernel<kSparseStream, 128>), g, b, 0, stream, args);
     else hipLaunchKernelGGL((decode_kernel<kSparseStream, 64>), g, b, 0, stream, args);
   } else if (args.num_shards > 1) {

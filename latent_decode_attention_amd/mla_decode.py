@@ -39,7 +39,11 @@ class Problem(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("block_table", ctypes.c_void_p),
                 ("max_blocks", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
-                ("max_seq_len", ctypes.c_int32), ("group_rows", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32), ("group_rows", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("kv_scale", ctypes.c_void_p)]
+
+
+MLA_KV_BF16, MLA_KV_INT8 = 0, 1
 
 
 class Plan(ctypes.Structure):
@@ -117,18 +121,26 @@ GROUP_ROWS = 0
 
 
 def make_problem(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
-                 scale: float, max_seq_len: int) -> Problem:
-    """mla_problem_t for q [B,Q,h_q,576] bf16, kv [N,bs,576] bf16, block_table [B,M] int32, seq_lens [B] int32."""
-    for name, t, dt, nd in (("q", q, torch.bfloat16, 4), ("kv", kv, torch.bfloat16, 3),
-                            ("block_table", block_table, torch.int32, 2), ("seq_lens", seq_lens, torch.int32, 1)):
+                 scale: float, max_seq_len: int, kv_scale: Optional[torch.Tensor] = None) -> Problem:
+    """mla_problem_t for q [B,Q,h_q,576] bf16, kv [N,bs,576] bf16 (or int8 with kv_scale fp32
+    [N,bs], one factor per cache row), block_table [B,M] int32, seq_lens [B] int32."""
+    kv_dt = torch.int8 if kv_scale is not None else torch.bfloat16
+    checks = [("q", q, torch.bfloat16, 4), ("kv", kv, kv_dt, 3),
+              ("block_table", block_table, torch.int32, 2), ("seq_lens", seq_lens, torch.int32, 1)]
+    if kv_scale is not None:
+        checks.append(("kv_scale", kv_scale, torch.float32, 2))
+    for name, t, dt, nd in checks:
         if t.dtype != dt or t.dim() != nd or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous {nd}-d {dt} tensor")
         if not t.is_cuda:
             raise TypeError(f"{name} must live on the GPU")
+    if kv_scale is not None and tuple(kv_scale.shape) != tuple(kv.shape[:2]):
+        raise TypeError("kv_scale must be [num_blocks, block_size]")
     B, Q, h_q, d_qk = q.shape
     return Problem(B, Q, h_q, d_qk, 512, float(scale), q.data_ptr(), kv.data_ptr(), kv.shape[0],
                    kv.shape[1], block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(),
-                   int(max_seq_len), int(GROUP_ROWS))
+                   int(max_seq_len), int(GROUP_ROWS), MLA_KV_BF16 if kv_scale is None else MLA_KV_INT8,
+                   None if kv_scale is None else kv_scale.data_ptr())
 
 
 def mla_workspace_size(problem: Problem, num_shards: int = 1, shard_id: int = -1, top_k: int = 0) -> int:
@@ -156,9 +168,11 @@ def _workspace(problem, num_shards, shard_id, top_k, workspace, device):
 def mla_decode_dense(q, kv, block_table, seq_lens, *, scale: float, max_seq_len: int,
                      num_shards: int = 1, interleave: int = 1, shard_id: int = -1,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Dense decode (optionally DCP-sharded).  Returns (out, lse)."""
-    p = make_problem(q, kv, block_table, seq_lens, scale, max_seq_len)
+                     out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None, stream=None,
+                     kv_scale: Optional[torch.Tensor] = None):
+    """Dense decode (optionally DCP-sharded).  Returns (out, lse).  With kv_scale the
+    cache is int8 and row r's values are kv_scale[r] * kv[r]."""
+    p = make_problem(q, kv, block_table, seq_lens, scale, max_seq_len, kv_scale)
     B, Q, h_q, _ = q.shape
     sharded = num_shards > 1
     n_out = (num_shards if shard_id < 0 else 1) if sharded else 1
@@ -184,11 +198,13 @@ def mla_decode_sparse(q, kv, block_table, seq_lens, indices, *, scale: float, ma
                       index_stride_q: Optional[int] = None, num_shards: int = 1, interleave: int = 1,
                       shard_id: int = -1, out: Optional[torch.Tensor] = None,
                       lse: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
-                      workspace: Optional[torch.Tensor] = None, stream=None):
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      kv_scale: Optional[torch.Tensor] = None):
     """Sparse top-k decode.  indices: int32, [B, top_k] (shared across Q) or [B, Q, top_k].
     With num_shards > 1 (mla_decode_sparse_dcp) each DCP shard attends the listed
-    positions it holds and emits fp32 partials [n_out, B, Q, h_q, 512] and lse."""
-    p = make_problem(q, kv, block_table, seq_lens, scale, max_seq_len)
+    positions it holds and emits fp32 partials [n_out, B, Q, h_q, 512] and lse.  With
+    kv_scale the cache is int8 (as in mla_decode_dense)."""
+    p = make_problem(q, kv, block_table, seq_lens, scale, max_seq_len, kv_scale)
     if indices.dtype != torch.int32 or not indices.is_contiguous() or not indices.is_cuda:
         raise TypeError("indices must be a contiguous int32 GPU tensor")
     B, Q, h_q, _ = q.shape

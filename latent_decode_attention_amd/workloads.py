@@ -25,7 +25,7 @@ Recipe (stated once here, used by every config):
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Optional
 
 import numpy as np
@@ -73,6 +73,10 @@ class Workload:
     num_shards: int = 1
     interleave: int = 1
     meta: dict = field(default_factory=dict)
+    # int8 latent cache (when set, the cache the workload describes): int8
+    # [num_blocks, block_size, 576] and one fp32 factor per row [num_blocks, block_size].
+    kv8: Optional[np.ndarray] = None
+    kv_scale: Optional[np.ndarray] = None
 
     @property
     def num_blocks(self) -> int:
@@ -201,6 +205,29 @@ def make_workload(name: str, B: int, Q: int, h_q: int, seq_lens, block_size: int
 # ---------------------------------------------------------------------------
 # The five decode workloads the method is measured on, plus the dense 32k point.
 # ---------------------------------------------------------------------------
+
+def int8_cache(w: Workload) -> Workload:
+    """The same workload over an int8 latent cache: each row of the bf16 cache
+    becomes int8 codes rint(x / f) with one fp32 factor f = max|x| / 127 per row
+    (codes in [-127, 127]; all-zero rows get f = 0).  Rows holding NaN (the
+    poisoned spare blocks) get code 0 and factor NaN, so they stay poison.  This
+    is an input recipe only: the method reads the codes and factors as given."""
+    nb, bs, d = w.kv.shape
+    kv8 = np.empty((nb, bs, d), dtype=np.int8)
+    fac = np.empty((nb, bs), dtype=np.float32)
+    step = max(1, (1 << 22) // (bs * d))
+    for s in range(0, nb, step):
+        e = min(nb, s + step)
+        x = bf16_bits_to_f32(w.kv[s:e])
+        bad = np.isnan(x).any(axis=2)
+        x = np.where(np.isnan(x), np.float32(0.0), x)
+        m = np.abs(x).max(axis=2)
+        f = (m / np.float32(127.0)).astype(np.float32)
+        safe = np.where(f > 0, f, np.float32(1.0))
+        kv8[s:e] = np.clip(np.rint(x / safe[:, :, None]), -127, 127).astype(np.int8)
+        fac[s:e] = np.where(bad, np.float32(np.nan), f)
+    return replace(w, name=w.name + "_kv8", kv8=kv8, kv_scale=fac)
+
 
 def config_tiny(seed: int = 1001) -> Workload:
     """Dense, B=1 Q=1 h_q=16 S=256, one contiguous 256-token block."""

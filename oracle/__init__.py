@@ -64,7 +64,8 @@ class _Problem(ctypes.Structure):
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("scale", ctypes.c_double),
                 ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("max_blocks", ctypes.c_int32), ("seq_lens", ctypes.c_void_p)]
+                ("max_blocks", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+                ("kv8", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p)]
 
 
 _ERRORS = {1: "bad argument", 2: "block table entry out of range", 3: "out of memory"}
@@ -83,8 +84,16 @@ def _problem(w, keep: list) -> _Problem:
     assert kv.ndim == 3 and kv.shape[2] == w.d_qk
     assert bt.ndim == 2 and bt.shape[0] == w.B and sl.shape == (w.B,)
     keep += [q, kv, bt, sl]
+    kv8 = fac = None
+    if getattr(w, "kv8", None) is not None:
+        # The workload's cache is int8: the oracle reads the codes and factors.
+        kv8 = np.ascontiguousarray(w.kv8, dtype=np.int8)
+        fac = np.ascontiguousarray(w.kv_scale, dtype=np.float32)
+        assert kv8.shape == kv.shape and fac.shape == kv.shape[:2]
+        keep += [kv8, fac]
     return _Problem(w.B, w.Q, w.h_q, w.d_qk, w.d_v, float(w.scale), q.ctypes.data, kv.ctypes.data,
-                    kv.shape[0], kv.shape[1], bt.ctypes.data, bt.shape[1], sl.ctypes.data)
+                    kv.shape[0], kv.shape[1], bt.ctypes.data, bt.shape[1], sl.ctypes.data,
+                    None if kv8 is None else kv8.ctypes.data, None if fac is None else fac.ctypes.data)
 
 
 def _sel(w, rows: Optional[Sequence[int]]):

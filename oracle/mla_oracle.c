@@ -60,6 +60,10 @@ typedef struct {
   const int32_t *block_table; /* [B, max_blocks] */
   int32_t max_blocks;
   const int32_t *seq_lens;    /* [B] */
+  /* int8 cache, used instead of kv when kv8 is non-null: codes [num_blocks,
+   * block_size, d_qk] and one factor per row [num_blocks, block_size]. */
+  const int8_t *kv8;
+  const float *kv_scale;
 } oracle_problem;
 
 /* bf16 is the upper half of an IEEE binary32; the widening to double is exact. */
@@ -68,6 +72,15 @@ static double bf16_value(uint16_t bits) {
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
+}
+
+/* Column c of latent cache row `row`.  bf16 cache: the stored value.  int8
+ * cache (the one-byte kv-int8 element type of the DCP page, notation table of
+ * §2.1.4 and the open items of §3.3; the pages leave its dequantisation open): the row's factor times the code, both
+ * exact in double. */
+static double latent_value(const oracle_problem *P, int64_t row, int c) {
+  if (P->kv8) return (double)P->kv_scale[row] * (double)P->kv8[row * P->d_qk + c];
+  return bf16_value(P->kv[row * P->d_qk + c]);
 }
 
 /* Physical cache row of logical position p of sequence b (table A of the DCP page). */
@@ -94,9 +107,8 @@ static int attend(const oracle_problem *P, int b, int qi, int h, const int64_t *
   for (int64_t j = 0; j < n; ++j) {
     int64_t row = physical_row(P, b, pos[j]);
     if (row < 0) return ORACLE_ERR_BLOCK;
-    const uint16_t *krow = P->kv + row * D;
     double dot = 0.0;
-    for (int k = 0; k < D; ++k) dot += bf16_value(qrow[k]) * bf16_value(krow[k]);
+    for (int k = 0; k < D; ++k) dot += bf16_value(qrow[k]) * latent_value(P, row, k);
     s[j] = P->scale * dot;
   }
   double m = s[0];
@@ -107,15 +119,17 @@ static int attend(const oracle_problem *P, int b, int qi, int h, const int64_t *
   /* O = sum_p softmax_p * v_p with v_p = the first d_v columns of the latent row */
   for (int64_t j = 0; j < n; ++j) {
     double w = exp(s[j] - m) / l;
-    const uint16_t *vrow = P->kv + physical_row(P, b, pos[j]) * D;
-    for (int c = 0; c < DV; ++c) out[c] += w * bf16_value(vrow[c]);
+    const int64_t vrow = physical_row(P, b, pos[j]);
+    for (int c = 0; c < DV; ++c) out[c] += w * latent_value(P, vrow, c);
   }
   *lse = m + log(l);
   return ORACLE_OK;
 }
 
 static int check_problem(const oracle_problem *P) {
-  if (!P || !P->q || !P->kv || !P->block_table || !P->seq_lens) return ORACLE_ERR_ARG;
+  if (!P || !P->q || (!P->kv && !P->kv8) || (P->kv8 && !P->kv_scale) || !P->block_table ||
+      !P->seq_lens)
+    return ORACLE_ERR_ARG;
   if (P->B <= 0 || P->Q <= 0 || P->h_q <= 0 || P->d_qk <= 0 || P->d_v <= 0 ||
       P->d_v > P->d_qk || P->block_size <= 0 || P->num_blocks <= 0 || P->max_blocks <= 0)
     return ORACLE_ERR_ARG;

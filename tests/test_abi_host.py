@@ -61,9 +61,21 @@ def dense_status(p, num_shards=1, interleave=1, shard_id=-1, out=FAKE, dtype=0, 
     (dict(max_seq_len=2049 + 31 * 64), 2), (dict(max_seq_len=0), 2), (dict(scale=float("nan")), 2),
     (dict(scale=0.0), 2), (dict(scale=-0.07), 2), (dict(group_rows=96), 2), (dict(group_rows=-64), 2),
     (dict(q=FAKE + 8), 2),
+    (dict(kv_dtype=1), 1), (dict(kv_dtype=2, kv_scale=FAKE), 3), (dict(kv_dtype=-1), 3),
+    (dict(kv_dtype=1, kv_scale=FAKE, group_rows=128), 3), (dict(kv_dtype=1, kv_scale=FAKE + 2), 2),
 ])
 def test_dense_validation_statuses(kw, status):
     assert dense_status(problem(**kw)) == status
+
+
+@pytest.mark.parametrize("h_q,Q,S", [(128, 1, 4096), (128, 1, 200000), (64, 2, 1000), (16, 1, 256)])
+def test_plan_int8_cache_takes_64_row_groups(h_q, Q, S):
+    p = problem(h_q=h_q, Q=Q, num_blocks=4096, max_blocks=4096, max_seq_len=S, kv_dtype=1, kv_scale=FAKE)
+    plan = md.mla_plan_query(p, num_cus=256)
+    assert plan["rows_per_group"] <= 64
+    # the bf16 plan of the same problem may take 128 rows; the int8 one never does
+    assert md.mla_plan_query(problem(h_q=h_q, Q=Q, num_blocks=4096, max_blocks=4096, max_seq_len=S,
+                                     kv_dtype=1, kv_scale=FAKE, group_rows=64), num_cus=256) == plan
 
 
 def test_dense_argument_statuses():

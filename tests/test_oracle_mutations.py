@@ -18,7 +18,13 @@ import test_oracle_pins as pins
 MUTATIONS = {
     "drop_scale": ("s[j] = P->scale * dot;", "s[j] = dot;"),
     "dot_over_v_columns_only": ("for (int k = 0; k < D; ++k) dot", "for (int k = 0; k < DV; ++k) dot"),
-    "v_from_wrong_columns": ("out[c] += w * bf16_value(vrow[c]);", "out[c] += w * bf16_value(vrow[c + 64]);"),
+    "v_from_wrong_columns": ("out[c] += w * latent_value(P, vrow, c);", "out[c] += w * latent_value(P, vrow, c + 64);"),
+    "kv8_factor_dropped": ("return (double)P->kv_scale[row] * (double)P->kv8[row * P->d_qk + c];",
+                           "return (double)P->kv8[row * P->d_qk + c];"),
+    "kv8_codes_unsigned": ("(double)P->kv8[row * P->d_qk + c]", "(double)(uint8_t)P->kv8[row * P->d_qk + c]"),
+    "kv8_factor_of_neighbour_row": ("P->kv_scale[row]", "P->kv_scale[row ^ 1]"),
+    "kv8_factor_on_keys_only": ("out[c] += w * latent_value(P, vrow, c);",
+                                "out[c] += w * (P->kv8 ? (double)P->kv8[vrow * D + c] : latent_value(P, vrow, c));"),
     "causal_off_by_one": ("for (int64_t p = 0; p <= last; ++p)", "for (int64_t p = 0; p < last; ++p)"),
     "sparse_no_causal_filter": ("if (i >= 0 && i <= last && (", "if (i >= 0 && i < P->seq_lens[b] && ("),
     "sparse_shard_rule_by_token": ("(i / interleave) % num_shards == shard_id", "i % num_shards == shard_id"),

@@ -376,3 +376,38 @@ def test_merge_weights_are_normalised_softmax_of_lse():
     w = softmax(l, axis=0)
     np.testing.assert_allclose(mo, np.einsum("nr,nrc->rc", w, o), atol=1e-13)
     np.testing.assert_allclose(ml, logsumexp(l, axis=0), atol=1e-13)
+
+
+# ---- int8 latent cache.  The pages name a one-byte cache element but no
+# dequantisation rule; the reading is value = (row factor) x (signed code).  Pin:
+# codes times power-of-two factors are exact bf16 numbers, so the oracle over
+# the int8 cache must give bit for bit what it gives over a bf16 cache holding
+# those values (the bf16 reading being pinned by everything above).  Random
+# per-row exponents catch a factor taken from the wrong row or dropped; codes
+# spanning [-128, 127] catch an unsigned reading.
+
+def _int8_pair(seed: int, per_row: bool, sparse: bool):
+    from dataclasses import replace
+    from latent_decode_attention_amd import workloads as W
+    w = W.make_workload("kv8pin", 2, 2, 16, [37, 100], 16, seed, top_k=48 if sparse else 0,
+                        shared_q_indices=False)
+    g = np.random.default_rng(seed)
+    codes = g.integers(-128, 128, size=w.kv.shape).astype(np.int8)
+    if per_row:
+        fac = (2.0 ** g.integers(-12, 3, size=w.kv.shape[:2])).astype(np.float32)
+    else:
+        fac = np.ones(w.kv.shape[:2], dtype=np.float32)
+    vals = codes.astype(np.float64) * fac[..., None].astype(np.float64)
+    kvb = bf16(vals.astype(np.float32))
+    assert np.array_equal(f64(kvb), vals), "the values must be exact in bf16 for this pin"
+    return replace(w, kv8=codes, kv_scale=fac), replace(w, kv=kvb)
+
+
+@pytest.mark.parametrize("per_row,sparse", [(False, False), (True, False), (True, True)])
+def test_int8_cache_equals_bf16_cache_of_the_same_values(per_row, sparse):
+    w8, wb = _int8_pair(41 + per_row + 2 * sparse, per_row, sparse)
+    run = oracle.sparse if sparse else oracle.dense
+    o8, l8 = run(w8)
+    ob, lb = run(wb)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+    assert np.isfinite(o8).all()
