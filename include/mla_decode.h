@@ -86,7 +86,7 @@ typedef struct {
                                  fewer.  Any other value: MLA_ERR_BAD_SHAPE */
   /*
    * Element type of the latent cache (the int8 cache is the one-byte "kv-int8"
-   * element type of "RFC: MsModeling 支持 Decode Context Parallel", the notation
+   * element type of "RFC: MsModeling 支持 Decode Context Parallel 仿真", the notation
    * table of §2.1.4, listed again among the open items of §3.3; the pages state
    * no dequantisation rule).  MLA_KV_BF16 (0, the default of a zeroed struct): `kv` holds bf16 and
    * `kv_scale` is ignored.  MLA_KV_INT8 (1): `kv` holds int8 and `kv_scale`
