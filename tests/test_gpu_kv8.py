@@ -19,7 +19,7 @@ import oracle  # noqa: E402
 from latent_decode_attention_amd import mla_decode as md  # noqa: E402
 from latent_decode_attention_amd import workloads as W  # noqa: E402
 from latent_decode_attention_amd.device import upload, run  # noqa: E402
-from test_gpu_parity import assert_lse_close, assert_o_close, sampled_rows  # noqa: E402
+from test_gpu_parity import EDGE_SHAPES, assert_lse_close, assert_o_close, sampled_rows  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,20 @@ def oracle_of(w, rows=None):
 def test_int8_cache_matches_the_oracle(name, out_dtype):
     w = CASES[name]()
     out, lse = run(upload(w), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle_of(w)
+    assert_o_close(out, ro, w.name)
+    assert_lse_close(lse, rl, w.name)
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_SHAPES))
+def test_int8_edge_shapes(name):
+    """The limits of the supported range (1, 3 and 96 heads, 16 query tokens, 1-
+    and 4096-token pages, a 65536-entry list, 600 sequences) over the int8 cache."""
+    B, Q, h, lens, bs, k, shared = EDGE_SHAPES[name]
+    w = W.int8_cache(W.make_workload(name, B, Q, h, lens, bs, seed=sum(map(ord, name)) + 1, top_k=k,
+                                     shared_q_indices=shared, spare_blocks=2))
+    out, lse = run(upload(w), out_dtype=torch.float32)
     torch.cuda.synchronize()
     ro, rl = oracle_of(w)
     assert_o_close(out, ro, w.name)
