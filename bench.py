@@ -313,13 +313,13 @@ def main():
     md.GROUP_ROWS = args.group_rows
     t0 = time.time()
     if args.top_k:
-        w = W.CONFIGS[args.config]()
+        w = W.PRESETS[args.config]()
         if w.indices is None or w.index_stride_q != 0:
             raise SystemExit("--top-k applies to the sparse presets with one list per sequence")
         w = W.make_workload(f"{w.name}_k{args.top_k}", w.B, w.Q, w.h_q, w.seq_lens, w.block_size,
                             int(w.meta["seed"]), top_k=args.top_k)
     else:
-        w = W.CONFIGS[args.config]()
+        w = W.PRESETS[args.config]()
     if args.kv == "int8":
         w = W.int8_cache(w)
     d = upload(w, dev)

@@ -274,7 +274,7 @@ def config_sparse_dcp(seed: int = 1007) -> Workload:
                          top_k=2048, num_shards=8, interleave=64)
 
 
-CONFIGS = {
+PRESETS = {
     1: config_tiny,
     2: config_dense_paged,
     3: config_sparse,

@@ -497,7 +497,7 @@ def sampled_rows(w, n, seed):
 @pytest.mark.parametrize("cfg,out_dtype", [(2, torch.bfloat16), (3, torch.bfloat16), (5, torch.bfloat16),
                                            (5, torch.float32), (6, torch.bfloat16)])
 def test_full_size_config_sampled(cfg, out_dtype):
-    w = W.CONFIGS[cfg]()
+    w = W.PRESETS[cfg]()
     d = upload(w)
     out, lse = run(d, out_dtype=out_dtype)
     torch.cuda.synchronize()
