@@ -104,14 +104,29 @@ static_assert(sizeof(Smem<128>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024,
 // constraints (scores in VGPRs, outputs in AGPRs) to keep the allocator from
 // shuffling them.  Hazards the compiler cannot see through the asm are covered
 // by the fences below (their s_nop counts exceed what the 32x32x16 MFMA needs).
+// kGuard: four wait states inside the asm, ahead of the MFMA.  Where the
+// register allocator parks operands in AGPRs it copies them back right before
+// the asm, too late for any fence in the source; the guard covers those copies.
+template <bool kGuard = false>
 __device__ __forceinline__ void mfma_vgpr_first(f32x16 &d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  if constexpr (kGuard)
+    asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
+template <bool kGuard = false>
 __device__ __forceinline__ void mfma_vgpr(f32x16 &d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  if constexpr (kGuard)
+    asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+template <bool kGuard = false>
 __device__ __forceinline__ void mfma_agpr(f32x16 &d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  if constexpr (kGuard)
+    asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 // Zero a 16-register accumulator tile without touching VGPRs: 0 x 0 + 0.
 __device__ __forceinline__ void acc_zero(f32x16 &d, bf16x8 z) {
@@ -792,10 +807,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           for (int st = 0; st < kQkSteps; ++st) {
             tile_step_work(sb * kQkSteps + st);
             if (st + kKAhead < kQkSteps) kr[(st + kKAhead) % (kKAhead + 1)] = k_read(st + kKAhead);
+            // (The int8 kernels run at the register limit, where the allocator
+            // parks query operands in AGPRs: their MFMAs carry the guard.)
             if (st == 0)
-              mfma_vgpr_first(s, kr[0], qr[0]);
+              mfma_vgpr_first<kKv8>(s, kr[0], qr[0]);
             else
-              mfma_vgpr(s, kr[st % (kKAhead + 1)], qr[st]);
+              mfma_vgpr<kKv8>(s, kr[st % (kKAhead + 1)], qr[st]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -915,7 +932,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           // write precedes the MFMA's operand read.
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[kb & 1][rt]);
+          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr<kKv8>(acc[4 * rt + ct], va, pr[kb & 1][rt]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
