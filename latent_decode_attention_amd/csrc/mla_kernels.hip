@@ -467,7 +467,8 @@ __device__ __forceinline__ void store_out(void *out, int kind, int64_t elem, f32
 // exact in bf16; the kernel takes the bias back out of the scores and outputs.
 // Pass (h, g) covers 8 rows x the 8 chunks of column group g: lane l reads 8 raw
 // bytes (512 contiguous bytes per wave) and writes one 16-byte chunk (each 16
-// lanes write two whole 128-byte rows: every bank once).
+// lanes write two whole 128-byte rows: every bank once).  The 9 reads of a half
+// are issued together, so their latency is paid twice per tile, not 18 times.
 __device__ __forceinline__ void widen_tile8(const char *raw_buf, char *tile_buf, int wave, int lane) {
   const char LDS_AS *src = (const char LDS_AS *)(raw_buf + wave * 16 * kRowBytes8 + 8 * lane);
   const int c = lane & 7;
@@ -475,10 +476,16 @@ __device__ __forceinline__ void widen_tile8(const char *raw_buf, char *tile_buf,
   for (int h = 0; h < 2; ++h) {
     const int rr = 8 * h + (lane >> 3);  // row within the wave's 16; its key is that of 16 wave + rr
     char LDS_AS *dst = (char LDS_AS *)(tile_buf + (16 * wave + rr) * 128 + 16 * (c ^ chunk_key(rr)));
+    unsigned rl[kGroups], rh[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
       const u32x2 w = *(const u32x2 LDS_AS *)(src + g * 1024 + h * 512);
-      const unsigned lo = w[0] ^ 0x80808080u, hi = w[1] ^ 0x80808080u;
+      rl[g] = w[0];
+      rh[g] = w[1];
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const unsigned lo = rl[g] ^ 0x80808080u, hi = rh[g] ^ 0x80808080u;
       const u32x4 o = {pack_bf16((float)(lo & 255u), (float)((lo >> 8) & 255u)),
                        pack_bf16((float)((lo >> 16) & 255u), (float)(lo >> 24)),
                        pack_bf16((float)(hi & 255u), (float)((hi >> 8) & 255u)),
