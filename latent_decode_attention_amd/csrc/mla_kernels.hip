@@ -939,7 +939,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           // write precedes the MFMA's operand read.
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr<kKv8>(acc[4 * rt + ct], va, pr[kb & 1][rt]);
+          // (Unguarded: V comes straight from the LDS reads and P from LDS; the
+          // hazard scan of the compiled kernels confirms no copy lands in front.)
+          for (int rt = 0; rt < kRowTiles; ++rt) mfma_agpr(acc[4 * rt + ct], va, pr[kb & 1][rt]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
