@@ -99,8 +99,33 @@ def stored_traffic(workload_name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_s: float, seed: int = 0):
-    """Time the fp64 oracle on a bounded sample of output rows of the same workload."""
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Parity bars (the contract): lse within 1e-3; O within 1e-2, for bf16 outputs
+# where |O_ref| < 4 (1 bf16 ulp of O_ref beyond, where rounding alone exceeds 1e-2).
+def _o_bar(o_ref, bf16_out):
+    if not bf16_out:
+        return np.full_like(o_ref, 1e-2)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 7)
+    return np.where(np.abs(o_ref) < 4.0, 1e-2, ulp)
+
+
+def cpu_baseline(w, target_s: float, gpu_out=None, seed: int = 0):
+    """Time the fp64 oracle on a bounded sample of output rows of the same workload.
+
+    gpu_out = (O [rows, 512] float64, lse [rows], bf16_out) of the GPU path on
+    the workload's own inputs: the rows the oracle computes on its first pass
+    over the workload are compared with them (max |dO|, max |dlse|, max |O_ref|)."""
     import oracle
     g = np.random.default_rng(seed)
     rows_all = g.permutation(w.rows)
@@ -108,6 +133,7 @@ def cpu_baseline(w, target_s: float, seed: int = 0):
     spent = 0.0
     done_rows = 0
     done_work = 0
+    err = dict(max_abs_dO=0.0, max_abs_dlse=0.0, max_abs_O_ref=0.0, rows_compared=0, within_bars=True)
     # Rows are taken in a seeded random order; a workload smaller than the time
     # budget is run again from the start, so the rate is measured over >= target_s.
     passes = 0
@@ -118,10 +144,20 @@ def cpu_baseline(w, target_s: float, seed: int = 0):
             passes += 1
         t0 = time.perf_counter()
         if w.indices is not None:
-            oracle.sparse(w, rows=sel)
+            ro, rl = oracle.sparse(w, rows=sel)
         else:
-            oracle.dense(w, rows=sel)
+            ro, rl = oracle.dense(w, rows=sel)
         spent += time.perf_counter() - t0
+        if gpu_out is not None and done_rows < w.rows:
+            go, gl, bf16_out = gpu_out
+            d_o = np.abs(go[sel] - ro)
+            both_inf = np.isneginf(gl[sel]) & np.isneginf(rl)
+            d_l = np.where(both_inf, 0.0, np.abs(gl[sel] - rl))
+            err["max_abs_dO"] = max(err["max_abs_dO"], float(d_o.max()))
+            err["max_abs_dlse"] = max(err["max_abs_dlse"], float(np.nanmax(d_l)))
+            err["max_abs_O_ref"] = max(err["max_abs_O_ref"], float(np.abs(ro).max()))
+            err["rows_compared"] += len(sel)
+            err["within_bars"] &= bool(np.all(d_o <= _o_bar(ro, bf16_out)) and np.all(d_l <= 1e-3))
         for r in sel:
             b = int(r) // (w.Q * w.h_q)
             qi = (int(r) // w.h_q) % w.Q
@@ -133,10 +169,33 @@ def cpu_baseline(w, target_s: float, seed: int = 0):
                 done_work += int(np.count_nonzero((lst >= 0) & (lst <= S - w.Q + qi)))
         done_rows += len(sel)
         n = min(n * 2, 4096)
-    return dict(value=done_work / spent, unit="KV-token·heads/s", cores=oracle.num_threads(),
-                kind="oracle",
-                sample=(f"{done_rows} output rows (b,q,head) of {w.name} ({w.rows} rows in all, "
-                        f"{passes} full passes), fp64, {spent:.1f} s"))
+    rec = dict(value=done_work / spent, unit="KV-token·heads/s", cores=oracle.num_threads(),
+               kind="oracle", cpu_model=cpu_model(),
+               sample=(f"{done_rows} output rows (b,q,head) of {w.name} ({w.rows} rows in all, "
+                       f"{passes} full passes), fp64, {spent:.1f} s"))
+    if gpu_out is not None:
+        rec["parity"] = err
+    return rec
+
+
+def measure_copy_gbs(torch, dev, mib: int = 1024, reps: int = 10) -> float:
+    """Device-to-device copy rate (bytes read + written per second) of a plain
+    torch copy of `mib` MiB: the bandwidth a streaming kernel reaches on this machine."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def run_kv_write(args, torch, md, W, dev):
@@ -342,7 +401,7 @@ def main():
                              top_k=w.top_k, index_stride_q=w.index_stride_q,
                              num_cus=torch.cuda.get_device_properties(dev).multi_processor_count)
     splits = plan["splits"]
-    ws_bytes = md.mla_workspace_size(p0, w.num_shards, -1, w.top_k)
+    ws_bytes = md.mla_workspace_size(p0, w.num_shards, w.interleave, -1, w.top_k, w.index_stride_q)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     sharded = w.num_shards > 1
     if sharded:
@@ -381,6 +440,19 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-step times: a second pass of K steps with an event pair around each
+    # (the median is robust to the odd slow step; the bracketed mean above is
+    # the reported rate).
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([e0.elapsed_time(e1) for e0, e1 in pairs])
 
     # One step is one library call: the decode kernel plus, when the planner
     # splits sequences into partitions (or for DCP shards), the merge kernel.
@@ -436,11 +508,24 @@ def main():
                      "mfma_frac": achieved_tfs / MFMA_BF16_PEAK_TFS,
                      "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"]},
     }
-    print(f"[bench] {ms_per_step * 1e3:.1f} us/step ({splits} partitions per unit), "
-          f"{achieved_gbs:.0f} GB/s algorithmic = {achieved_gbs / HBM_PEAK_GBS:.3f} of HBM peak",
+    rec["timing"] = {"mean_ms": ms_per_step, "median_ms": float(np.median(per_step)),
+                     "min_ms": float(per_step.min()), "max_ms": float(per_step.max()),
+                     "per_step_events_mean_ms": float(per_step.mean())}
+    copy_gbs = measure_copy_gbs(torch, dev)
+    rec["roofline"]["copy_gbs"] = copy_gbs
+    rec["roofline"]["frac_of_copy"] = achieved_gbs / copy_gbs
+    print(f"[bench] {ms_per_step * 1e3:.1f} us/step (median {np.median(per_step) * 1e3:.1f}; {splits} partitions "
+          f"per unit), {achieved_gbs:.0f} GB/s algorithmic = {achieved_gbs / HBM_PEAK_GBS:.3f} of HBM peak, "
+          f"{achieved_gbs / copy_gbs:.3f} of the measured copy rate ({copy_gbs:.0f} GB/s)",
           file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # The GPU result on the workload's own inputs, for the CPU leg's comparison.
+        step(0)
+        torch.cuda.synchronize()
+        o_res, l_res = (merged, mlse) if sharded else (out, lse)
+        gpu_out = (o_res.float().cpu().numpy().astype(np.float64).reshape(-1, 512),
+                   l_res.float().cpu().numpy().astype(np.float64).reshape(-1), o_res.dtype == torch.bfloat16)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, gpu_out)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

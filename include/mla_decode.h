@@ -25,9 +25,11 @@
  *  - Pointers marked "device" are HIP device pointers; the library reads and
  *    writes them only from kernels enqueued on `stream` (a hipStream_t; NULL
  *    is the null stream).  The caller owns every buffer.  The library never
- *    allocates, frees or synchronizes, keeps no state between calls, and is
- *    safe to call from several host threads (calls on one stream run in order;
- *    calls that share an output or workspace buffer on different streams race).
+ *    allocates, frees or synchronizes, and is safe to call from several host
+ *    threads (calls on one stream run in order; calls that share an output or
+ *    workspace buffer on different streams race).  The only state it keeps is
+ *    what it learns of each device on its first call there (the architecture,
+ *    checked to be gfx950, and the compute-unit count).
  *  - Arrays are dense, row-major, with the shapes given below.
  *  - Arguments are checked on the host before anything is enqueued; a failed
  *    check returns its status and enqueues nothing (the failure rules of the
@@ -55,7 +57,8 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (e.g. d_qk != 576) */
   MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < mla_workspace_size(...) */
   MLA_ERR_LAUNCH = 5,              /* the HIP runtime rejected a kernel launch */
-  MLA_ERR_DEVICE = 6               /* no usable gfx950 device for the current HIP device */
+  MLA_ERR_DEVICE = 6               /* the current HIP device is missing or not a gfx950 (checked
+                                      on the host once per device, before any launch) */
 } mla_status_t;
 
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
@@ -105,14 +108,24 @@ typedef enum { MLA_KV_BF16 = 0, MLA_KV_INT8 = 1 } mla_kv_dtype_t;
 /*
  * Bytes of scratch the decode call needs for its split-KV partial results
  * (fp32 partial outputs plus their lse) and, for sparse calls under DCP, for
- * each shard's part of the index lists.  `top_k` = 0 sizes a dense call,
- * > 0 a sparse call with that list length; `num_shards`/`shard_id` as in
- * mla_decode_dense (num_shards > 1 with top_k > 0 sizes mla_decode_sparse_dcp).  Depends on the current HIP device's compute-unit count
- * (256 is assumed when no device is visible).  Returns 0 when the plan needs
- * no scratch, and (size_t)-1 when the arguments are invalid.
+ * each shard's part of the index lists.  Pass the arguments the decode call
+ * will get; the size is that of the very plan the call makes:
+ *  num_shards, interleave, shard_id  as in mla_decode_dense / mla_decode_sparse_dcp
+ *              (1, any, any for an unsharded call).  The interleave matters: the
+ *              shard streams of a dense DCP call are runs of `interleave` tokens
+ *              dealt round-robin ("RFC: MsModeling 支持 Decode Context Parallel
+ *              仿真", §2.1.4.1), so the longest stream, and the partitions cut
+ *              from it, depend on it.
+ *  top_k       0 for a dense call, else the sparse call's list length.
+ *  index_stride_q  the sparse call's stride between query tokens (0 = one list
+ *              shared by the query tokens); ignored for dense calls.  >= 0.
+ * Depends on the current HIP device's compute-unit count (256 is assumed when
+ * no device is visible).  Returns 0 when the plan needs no scratch, and
+ * (size_t)-1 when the arguments are invalid.  Equal to
+ * mla_plan_query(...).workspace_bytes for the same arguments and num_cus.
  */
-size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards,
-                          int32_t shard_id, int32_t top_k);
+size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards, int32_t interleave,
+                          int32_t shard_id, int32_t top_k, int64_t index_stride_q);
 
 /*
  * Dense decode: A(b, q) = { p : 0 <= p <= S_b - Q + q }.
@@ -135,7 +148,8 @@ size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards,
  *              shard_id = -1, else 1 (out_dtype must be MLA_DTYPE_FP32).
  *  lse         device, fp32 [B, Q, h_q] (unsharded) or [n_out, B, Q, h_q].
  *  workspace   device scratch of workspace_bytes >= mla_workspace_size(problem,
- *              num_shards, shard_id, 0); may be NULL when that size is 0.
+ *              num_shards, interleave, shard_id, 0, 0); may be NULL when that
+ *              size is 0.
  */
 mla_status_t mla_decode_dense(const mla_problem_t *problem, int32_t num_shards,
                               int32_t interleave, int32_t shard_id, void *out,
@@ -157,7 +171,7 @@ mla_status_t mla_decode_dense(const mla_problem_t *problem, int32_t num_shards,
  *  index_stride_b  elements between sequences, >= 0.
  *  index_stride_q  elements between query tokens; 0 shares one list across Q.
  *  out, lse        as the unsharded dense call.
- *  workspace       >= mla_workspace_size(problem, 1, -1, top_k) bytes.
+ *  workspace       >= mla_workspace_size(problem, 1, 1, -1, top_k, index_stride_q) bytes.
  */
 mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indices,
                                int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
@@ -179,8 +193,9 @@ mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indi
  *              shard, or -1 for all shards in one call.
  *  out         device, fp32 [n_out, B, Q, h_q, 512], n_out = num_shards if
  *              shard_id = -1, else 1;  lse  device, fp32 [n_out, B, Q, h_q].
- *  workspace   >= mla_workspace_size(problem, num_shards, shard_id, top_k) bytes
- *              (never 0: it holds each shard's part of every list).
+ *  workspace   >= mla_workspace_size(problem, num_shards, interleave, shard_id, top_k,
+ *              index_stride_q) bytes (never 0: it holds each shard's part of
+ *              every list).
  *
  * The call first splits every list by owner shard (in list order) into the
  * workspace, then each shard streams only its own part; partitions are cut for

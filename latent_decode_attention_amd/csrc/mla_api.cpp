@@ -14,6 +14,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/mla_decode.h"
 #include "mla_internal.h"
@@ -191,12 +193,49 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   return MLA_OK;
 }
 
+// What the library learns about a device the first time a call runs on it:
+// whether it is a gfx950 (the only target the kernels are built for) and its
+// compute-unit count.  Looked up once per device under a lock, then read
+// without one.
+constexpr int kMaxDevices = 64;
+struct DeviceState {
+  std::atomic<int> state{0};  // 0: not looked at yet, 1: usable gfx950, -1: not usable
+  int cus = kDefaultCus;
+};
+DeviceState g_devices[kMaxDevices];
+std::mutex g_devices_mu;
+
+// The current HIP device, if it is a usable gfx950: MLA_OK and its state.
+mla_status_t current_device(DeviceState **out, int *dev_out = nullptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  DeviceState &d = g_devices[dev];
+  int st = d.state.load(std::memory_order_acquire);
+  if (st == 0) {
+    std::lock_guard<std::mutex> lock(g_devices_mu);
+    st = d.state.load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      st = -1;
+      if (hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+          (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':')) {
+        d.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kDefaultCus;
+        st = 1;
+      }
+      d.state.store(st, std::memory_order_release);
+    }
+  }
+  if (st < 0) return MLA_ERR_DEVICE;
+  *out = &d;
+  if (dev_out) *dev_out = dev;
+  return MLA_OK;
+}
+
+// Compute units the plan is sized for: the current device's, or 256 (MI355X)
+// when no usable device is visible (host-only size and plan queries).
 int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return kDefaultCus;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    return kDefaultCus;
-  return n;
+  DeviceState *d;
+  return current_device(&d) == MLA_OK ? d->cus : kDefaultCus;
 }
 
 mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int32_t *indices,
@@ -209,6 +248,8 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return MLA_ERR_BAD_SHAPE;
   }
   if (reinterpret_cast<uintptr_t>(out) & 15) return MLA_ERR_BAD_SHAPE;
+  DeviceState *dev;
+  if (current_device(&dev) != MLA_OK) return MLA_ERR_DEVICE;
   DecodeArgs a;
   std::memset(&a, 0, sizeof a);
   a.q = static_cast<const uint16_t *>(p->q);
@@ -301,13 +342,15 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
 
 extern "C" {
 
-size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards, int32_t shard_id,
-                          int32_t top_k) {
+size_t mla_workspace_size(const mla_problem_t *problem, int32_t num_shards, int32_t interleave,
+                          int32_t shard_id, int32_t top_k, int64_t index_stride_q) {
   if (check_problem(problem) != MLA_OK) return (size_t)-1;
+  if (index_stride_q < 0) return (size_t)-1;
   Plan pl;
-  // A shared index list never plans fewer partitions than per-token lists, so
-  // its size covers both.
-  if (make_plan(problem, num_shards, 1, shard_id, top_k, 0, device_cus(), &pl) != MLA_OK)
+  // The very plan the decode call makes for these arguments (the interleave
+  // sets the longest shard stream, the list stride whether query tokens share
+  // a work-group), so the size is exact.
+  if (make_plan(problem, num_shards, interleave, shard_id, top_k, index_stride_q, device_cus(), &pl) != MLA_OK)
     return (size_t)-1;
   return pl.ws_total;
 }
@@ -368,6 +411,8 @@ mla_status_t mla_topk_select(const float *scores, int64_t stride_b, int64_t stri
   if (B < 1 || Q < 1 || Q > 16 || max_len < 1 || top_k < 1 || top_k > kMaxTopK || stride_b < 0 ||
       stride_q < 0 || (int64_t)B * Q > INT32_MAX)
     return MLA_ERR_BAD_SHAPE;
+  DeviceState *dev;
+  if (current_device(&dev) != MLA_OK) return MLA_ERR_DEVICE;
   TopkArgs a;
   a.scores = scores;
   a.stride_b = stride_b;
@@ -392,6 +437,8 @@ mla_status_t mla_merge_lse(const float *o_parts, const float *lse_parts, int32_t
   if ((reinterpret_cast<uintptr_t>(o_parts) | reinterpret_cast<uintptr_t>(out)) & 15)
     return MLA_ERR_BAD_SHAPE;
   if (rows == 0) return MLA_OK;
+  DeviceState *dev;
+  if (current_device(&dev) != MLA_OK) return MLA_ERR_DEVICE;
   MergeArgs m;
   m.o_parts = o_parts;
   m.lse_parts = lse_parts;
@@ -417,6 +464,8 @@ mla_status_t mla_kv_write(const void *rows, const int32_t *slot_mapping, int64_t
   if (T == 0) return MLA_OK;
   if (!rows || !slot_mapping || !kv || (num_shards > 1 && !positions)) return MLA_ERR_NULL_POINTER;
   if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(kv)) & 15) return MLA_ERR_BAD_SHAPE;
+  DeviceState *dev;
+  if (current_device(&dev) != MLA_OK) return MLA_ERR_DEVICE;
   KvWriteArgs a;
   a.rows = rows;
   a.slots = slot_mapping;

@@ -63,7 +63,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Problem)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-    lib.mla_workspace_size.argtypes = [P, i32, i32, i32]
+    lib.mla_workspace_size.argtypes = [P, i32, i32, i32, i32, i64]
     lib.mla_workspace_size.restype = sz
     lib.mla_decode_dense.argtypes = [P, i32, i32, i32, vp, i32, vp, vp, sz, vp]
     lib.mla_decode_dense.restype = ctypes.c_int
@@ -143,8 +143,9 @@ def make_problem(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, s
                    None if kv_scale is None else kv_scale.data_ptr())
 
 
-def mla_workspace_size(problem: Problem, num_shards: int = 1, shard_id: int = -1, top_k: int = 0) -> int:
-    n = lib.mla_workspace_size(ctypes.byref(problem), num_shards, shard_id, top_k)
+def mla_workspace_size(problem: Problem, num_shards: int = 1, interleave: int = 1, shard_id: int = -1,
+                       top_k: int = 0, index_stride_q: int = 0) -> int:
+    n = lib.mla_workspace_size(ctypes.byref(problem), num_shards, interleave, shard_id, top_k, index_stride_q)
     if n == ctypes.c_size_t(-1).value:
         raise MlaError(2, "mla_workspace_size: invalid arguments")
     return int(n)
@@ -158,8 +159,8 @@ def mla_plan_query(problem: Problem, num_shards: int = 1, interleave: int = 1, s
     return plan.as_dict()
 
 
-def _workspace(problem, num_shards, shard_id, top_k, workspace, device):
-    need = mla_workspace_size(problem, num_shards, shard_id, top_k)
+def _workspace(problem, num_shards, interleave, shard_id, top_k, index_stride_q, workspace, device):
+    need = mla_workspace_size(problem, num_shards, interleave, shard_id, top_k, index_stride_q)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     return workspace
@@ -186,7 +187,7 @@ def mla_decode_dense(q, kv, block_table, seq_lens, *, scale: float, max_seq_len:
         lse = torch.empty(lshape, dtype=torch.float32, device=q.device)
     if tuple(out.shape) != oshape or tuple(lse.shape) != lshape or lse.dtype != torch.float32:
         raise TypeError("out/lse have the wrong shape or dtype")
-    workspace = _workspace(p, num_shards, shard_id, 0, workspace, q.device)
+    workspace = _workspace(p, num_shards, interleave, shard_id, 0, 0, workspace, q.device)
     _check(lib.mla_decode_dense(ctypes.byref(p), num_shards, interleave, shard_id, _ptr(out),
                                 _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
                                 0 if workspace is None else workspace.numel(), _stream(stream)))
@@ -226,7 +227,7 @@ def mla_decode_sparse(q, kv, block_table, seq_lens, indices, *, scale: float, ma
         if (tuple(out.shape) != (n_out, B, Q, h_q, 512) or out.dtype != torch.float32 or
                 tuple(lse.shape) != (n_out, B, Q, h_q) or lse.dtype != torch.float32):
             raise TypeError("sharded out/lse must be fp32 [n_out, B, Q, h_q, 512] and [n_out, B, Q, h_q]")
-        workspace = _workspace(p, num_shards, shard_id, top_k, workspace, q.device)
+        workspace = _workspace(p, num_shards, interleave, shard_id, top_k, index_stride_q, workspace, q.device)
         _check(lib.mla_decode_sparse_dcp(ctypes.byref(p), _ptr(indices), top_k, index_stride_b,
                                          index_stride_q, num_shards, interleave, shard_id, _ptr(out),
                                          _ptr(lse), _ptr(workspace),
@@ -236,7 +237,7 @@ def mla_decode_sparse(q, kv, block_table, seq_lens, indices, *, scale: float, ma
         out = torch.empty((B, Q, h_q, 512), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Q, h_q), dtype=torch.float32, device=q.device)
-    workspace = _workspace(p, 1, -1, top_k, workspace, q.device)
+    workspace = _workspace(p, 1, 1, -1, top_k, index_stride_q, workspace, q.device)
     _check(lib.mla_decode_sparse(ctypes.byref(p), _ptr(indices), top_k, index_stride_b, index_stride_q,
                                  _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
                                  0 if workspace is None else workspace.numel(), _stream(stream)))

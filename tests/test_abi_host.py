@@ -170,15 +170,15 @@ def test_plan_sparse_shards():
     assert pl["splits"] * pl["chunk"] >= 256
     lists = 8 * 1 * 8 * 2048 * 4
     assert pl["workspace_bytes"] >= lists
-    assert md.mla_workspace_size(pr, 8, -1, 2048) == pl["workspace_bytes"]
+    assert md.mla_workspace_size(pr, 8, 64, -1, 2048) == pl["workspace_bytes"]
     one = plan(pr, top_k=2048, num_shards=8, interleave=64, shard_id=3)
     assert one["stream_len"] == 256 and one["units"] == 8 * (128 // one["rows_per_group"])
-    assert md.mla_workspace_size(pr, 8, 3, 2048) >= 8 * 2048 * 4
+    assert md.mla_workspace_size(pr, 8, 64, 3, 2048) >= 8 * 2048 * 4
     # short sequences bound the share: S = 1000 < top_k, 3 shards -> 334
     short = plan(problem(B=8, max_seq_len=1000, max_blocks=16), top_k=2048, num_shards=3, interleave=7)
     assert short["stream_len"] == 334
     # per-token lists (Q = 2) are sized for as well
-    assert md.mla_workspace_size(problem(B=8, Q=2, max_seq_len=4096, max_blocks=64), 4, -1, 512) >= 8 * 2 * 4 * 512 * 4
+    assert md.mla_workspace_size(problem(B=8, Q=2, max_seq_len=4096, max_blocks=64), 4, 64, -1, 512, 512) >= 8 * 2 * 4 * 512 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -234,3 +234,83 @@ def test_topk_argument_checks(kw, status):
     a.update(kw)
     assert lib.mla_topk_select(a["scores"], a["stride_b"], a["stride_q"], a["seq_lens"], a["B"], a["Q"],
                                a["max_len"], a["top_k"], a["out"], None) == status
+
+
+def _sweep_cases():
+    """(problem kwargs, num_shards, interleave, shard_id, top_k, index_stride_q) over
+    sizes around tile and block boundaries, every interleave class (smaller than,
+    equal to and larger than a tile, larger than the sequence), each shard and
+    all shards, dense and sparse, shared and per-token lists, both group shapes."""
+    cases = []
+    for B in (1, 4, 32):
+        for S in (300, 2049, 4096, 70001):
+            mb = (S + 63) // 64
+            for Q, h in ((1, 128), (2, 64), (4, 16)):
+                for gr in (0, 64, 128):
+                    pk = dict(B=B, Q=Q, h_q=h, max_seq_len=S, max_blocks=mb, num_blocks=mb * B + 8,
+                              group_rows=gr)
+                    cases.append((pk, 1, 1, -1, 0, 0))
+                    for k in (64, 2048):
+                        cases.append((pk, 1, 1, -1, k, 0))
+                        cases.append((pk, 1, 1, -1, k, k))
+                    for N in (2, 4, 8):
+                        for I in (1, 7, 64, 128, 512, 1024):
+                            for r in (-1, 0, N - 1):
+                                cases.append((pk, N, I, r, 0, 0))
+                                cases.append((pk, N, I, r, 2048, 2048 if Q > 1 else 0))
+    return cases
+
+
+def test_workspace_size_is_the_plan_size_everywhere():
+    """mla_workspace_size gives exactly what the decode call's plan needs, for
+    every interleave (dense DCP shard streams depend on it), shard choice, list
+    length and list stride."""
+    bad = []
+    for pk, N, I, r, k, sq in _sweep_cases():
+        p = problem(**pk)
+        pl = plan(p, num_shards=N, interleave=I, shard_id=r, top_k=k, index_stride_q=sq, num_cus=256)
+        ws = md.mla_workspace_size(p, N, I, r, k, sq)
+        if ws != pl["workspace_bytes"]:
+            bad.append((pk, N, I, r, k, sq, ws, pl["workspace_bytes"]))
+    assert not bad, f"{len(bad)} mismatches, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("S,N,I,B", [(2049, 4, 1024, 1), (2049, 8, 512, 4), (300, 2, 512, 1)])
+def test_workspace_size_covers_large_interleaves(S, N, I, B):
+    """Shapes whose shard streams are long only because the interleave is large:
+    one run of I tokens holds most of the sequence."""
+    p = problem(B=B, h_q=16 if S == 300 else 128, max_seq_len=S, max_blocks=(S + 63) // 64)
+    need = plan(p, num_shards=N, interleave=I, shard_id=-1, num_cus=256)["workspace_bytes"]
+    assert need > 0
+    assert md.mla_workspace_size(p, N, I, -1, 0, 0) == need
+
+
+def test_workspace_size_rejects_bad_arguments():
+    invalid = ctypes.c_size_t(-1).value
+    p = problem()
+    assert lib.mla_workspace_size(ctypes.byref(p), 4, 0, -1, 0, 0) == invalid      # interleave 0
+    assert lib.mla_workspace_size(ctypes.byref(p), 4, 64, 4, 0, 0) == invalid      # shard out of range
+    assert lib.mla_workspace_size(ctypes.byref(p), 1, 1, -1, -5, 0) == invalid     # negative top_k
+    assert lib.mla_workspace_size(ctypes.byref(p), 1, 1, -1, 64, -1) == invalid    # negative stride
+    assert lib.mla_workspace_size(ctypes.byref(problem(d_qk=512)), 1, 1, -1, 0, 0) == invalid
+
+
+def _usable_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_usable_gpu(), reason="checks the status where no GPU is visible")
+def test_valid_calls_without_a_device_return_mla_err_device():
+    """Every argument is valid, so the only thing left to fail is the device:
+    the call says so (MLA_ERR_DEVICE) instead of reporting a launch failure."""
+    p = problem(B=512, max_seq_len=4096, max_blocks=64)   # no partitions: needs no workspace
+    assert plan(p)["workspace_bytes"] == 0
+    assert lib.mla_decode_dense(ctypes.byref(p), 1, 1, -1, FAKE, 0, FAKE, None, 0, None) == 6
+    assert lib.mla_decode_sparse(ctypes.byref(p), FAKE, 64, 64, 0, FAKE, 0, FAKE, None, 0, None) == 6
+    assert lib.mla_merge_lse(FAKE, FAKE, 2, 4, 512, FAKE, 1, FAKE, None) == 6
+    assert lib.mla_topk_select(FAKE, 4096, 2048, FAKE, 2, 2, 2048, 64, FAKE, None) == 6
+    assert lib.mla_kv_write(FAKE, FAKE, 10, FAKE, 100, FAKE, 1, 1, 0, None) == 6

@@ -2,11 +2,13 @@
 the fp64 oracle, which reads the same int8 codes and per-row factors (value =
 factor x code).
 
-Tolerances as for the bf16 cache (lse |Δ| <= 1e-3; O |Δ| <= 1e-2, plus half a
-bf16 ulp for bf16 outputs).  The kernel widens the codes exactly (as code + 128
-in bf16) and removes the bias in fp32, so the only roundings beyond the bf16
-cache's are fp32 ones and the bf16 rounding of the factor-carrying P.V weights
-(relative 2^-9 per weight, averaging out over the attended tokens).
+Bars as for the bf16 cache (tests/parity.py: lse |Δ| <= 1e-3; O |Δ| <= 1e-2,
+and for bf16 outputs 1 bf16 ulp where |O_ref| >= 4).  The kernel widens the
+codes exactly (as code + 128 in bf16) and removes the bias in fp32, so the only
+roundings beyond the bf16 cache's are fp32 ones and the bf16 rounding of the
+factor-carrying P.V weights (relative 2^-9 per weight, averaging out over the
+attended tokens).  The full-size workload over the int8 cache is compared on
+every row in test_gpu_full_size.py.
 """
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ import oracle  # noqa: E402
 from latent_decode_attention_amd import mla_decode as md  # noqa: E402
 from latent_decode_attention_amd import workloads as W  # noqa: E402
 from latent_decode_attention_amd.device import upload, run  # noqa: E402
-from test_gpu_parity import EDGE_SHAPES, assert_lse_close, assert_o_close, sampled_rows  # noqa: E402
+from test_gpu_parity import EDGE_SHAPES, assert_lse_close, assert_o_close  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -150,17 +152,3 @@ def test_int8_repeated_runs_are_bitwise_identical():
     b = run(d)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
-
-
-def test_int8_full_size_sparse_config_sampled():
-    # The sparse workload (B=32 Q=1 h_q=128 S=32768 top_k=2048) over the int8
-    # cache, in the launch configuration the benchmark times.
-    w = W.int8_cache(W.config_sparse())
-    out, lse = run(upload(w))
-    torch.cuda.synchronize()
-    rows = sampled_rows(w, 48, 3)
-    idx = torch.from_numpy(rows).cuda()
-    ro, rl = oracle.sparse(w, rows=rows)
-    assert_o_close(out.reshape(-1, 512)[idx], ro, w.name)
-    assert_lse_close(lse.reshape(-1)[idx], rl, w.name)
-    assert torch.isfinite(out.float()).all()

@@ -1,14 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
-Tolerances (fp32 accumulation, scores exact up to fp32 summation):
-  * lse: |Δ| <= 1e-3;
-  * O in fp32: |Δ| <= 1e-2;
-  * O in bf16: |Δ| <= 1e-2 + half a bf16 ulp at |O_ref| + 1e-2.  The result is
-    computed in fp32 (held to 1e-2 by the fp32 runs) and then rounded to
-    nearest bf16, which by itself moves it by up to half an ulp: 0.0078 at
-    |O| in [2, 4), more than 1e-2 beyond 4.
-Index and gather semantics (which positions are attended, -1 padding, block-table
-mapping) are checked exactly with one-hot probes and bitwise invariances.
+Bars (tests/parity.py): lse |Δ| <= 1e-3; O |Δ| <= 1e-2 for fp32 outputs, and
+for bf16 outputs where |O_ref| < 4 (1 bf16 ulp of O_ref beyond, where rounding
+alone can exceed 1e-2).  Index and gather semantics (which positions are
+attended, -1 padding, block-table mapping) are checked exactly with one-hot
+probes and bitwise invariances.  The full-size workloads are compared on every
+row in test_gpu_full_size.py.
 """
 import math
 
@@ -20,6 +17,7 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import oracle  # noqa: E402
+import parity  # noqa: E402
 from helpers import bf16, f64, random_rows, workload  # noqa: E402
 from latent_decode_attention_amd import mla_decode as md  # noqa: E402
 from latent_decode_attention_amd import workloads as W  # noqa: E402
@@ -37,30 +35,12 @@ def group_rows(request):
     md.GROUP_ROWS = 0
 
 
-def ulp_bf16(x):
-    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
-    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+def assert_o_close(o_gpu, o_ref, what="", label=None):
+    return parity.check_o(o_gpu, o_ref, what, label=label)
 
 
-def assert_o_close(o_gpu, o_ref, what=""):
-    g = o_gpu.float().cpu().numpy().astype(np.float64).reshape(o_ref.shape)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
-    err = np.abs(g - o_ref)
-    if o_gpu.dtype == torch.bfloat16:
-        tol = 1e-2 + 0.5 * ulp_bf16(np.abs(o_ref) + 1e-2)
-    else:
-        tol = np.full_like(o_ref, 1e-2)
-    bad = err > tol
-    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.3g}"
-    return float(err.max())
-
-
-def assert_lse_close(l_gpu, l_ref, what=""):
-    g = l_gpu.float().cpu().numpy().astype(np.float64).reshape(l_ref.shape)
-    both_inf = np.isneginf(g) & np.isneginf(l_ref)
-    err = np.where(both_inf, 0.0, np.abs(g - l_ref))
-    assert np.all(err <= 1e-3), f"{what}: lse max err {np.nanmax(err):.3g}"
-    return float(err.max())
+def assert_lse_close(l_gpu, l_ref, what="", label=None):
+    return parity.check_lse(l_gpu, l_ref, what, label=label)
 
 
 def oracle_of(w, rows=None, shard=None):
@@ -485,76 +465,41 @@ def test_empty_sequences_and_fully_masked_rows():
     assert_lse_close(lse, rl)
 
 
-# ---------------------------------------------------------------- full-size configs (sampled rows)
-
-def sampled_rows(w, n, seed):
-    g = np.random.default_rng(seed)
-    rows = set(g.choice(w.rows, size=min(n, w.rows), replace=False).tolist())
-    rows |= {0, w.rows - 1}
-    return np.array(sorted(rows), dtype=np.int64)
-
-
-@pytest.mark.parametrize("cfg,out_dtype", [(2, torch.bfloat16), (3, torch.bfloat16), (5, torch.bfloat16),
-                                           (5, torch.float32), (6, torch.bfloat16)])
-def test_full_size_config_sampled(cfg, out_dtype):
-    w = W.PRESETS[cfg]()
+def test_fp16_partials_meet_the_contract_bar():
+    """bf16-output calls keep split-KV partials as fp16 with a power-of-two scale
+    per (row, 128-column quarter).  Two sequences of N(0,1) rows are cut into
+    many partitions, so most of every output row passes through fp16 partials
+    and the merge: the result still meets the contract bar, and stays within
+    the partials' storage step of the fp32-partial (fp32 output) result."""
+    w = W.make_workload("fp16_partials_b2_h128_s2048", 2, 1, 128, [2048, 1300], 64, seed=43)
     d = upload(w)
-    out, lse = run(d, out_dtype=out_dtype)
+    pl = md.mla_plan_query(md.make_problem(d.q, d.kv, d.block_table, d.seq_lens, w.scale, w.max_seq_len))
+    assert pl["splits"] > 8
+    ob, lb = run(d, out_dtype=torch.bfloat16)
+    of, lf = run(d, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = sampled_rows(w, 48, cfg)
-    ro, rl = oracle_of(w, rows=rows)
-    og = out.reshape(-1, 512)[torch.from_numpy(rows).cuda()]
-    lg = lse.reshape(-1)[torch.from_numpy(rows).cuda()]
-    assert_o_close(og, ro, w.name)
-    assert_lse_close(lg, rl, w.name)
-    assert torch.isfinite(out.float()).all()
+    ro, rl = oracle.dense(w)
+    assert_o_close(ob, ro, "fp16 partials, bf16 out")
+    assert_o_close(of, ro, "fp32 partials, fp32 out")
+    assert_lse_close(lb, rl, "bf16 out")
+    assert_lse_close(lf, rl, "fp32 out")
+    g_b = ob.float().cpu().numpy().reshape(ro.shape).astype(np.float64)
+    g_f = of.float().cpu().numpy().reshape(ro.shape).astype(np.float64)
+    # fp16 keeps 11 significant bits of each partial's quarter-row maximum (a
+    # convex combination of V rows, so at most max|V|); the bf16 result then
+    # rounds to 8 bits
+    v_max = float(np.nanmax(np.abs(bf16_bits_to_f32(w.kv[..., :512]))))  # spare blocks hold NaN
+    assert np.all(np.abs(g_b - g_f) <= 2.0 ** -11 * v_max + parity.ulp_bf16(np.abs(g_f) * 1.001) * 0.5 + 1e-6)
 
 
-def test_full_size_split_kv_config_sampled():
-    w = W.config_split_kv()
-    d = upload(w)
-    parts, lses = run(d)
-    merged, mlse = md.mla_merge_lse(parts, lses, out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    rows = sampled_rows(w, 24, 4)
-    idx = torch.from_numpy(rows).cuda()
-    for r in (0, 5):
-        ro, rl = oracle.dense(w, rows=rows, num_shards=8, interleave=64, shard_id=r)
-        assert_o_close(parts[r].reshape(-1, 512)[idx], ro, f"shard {r}")
-        assert_lse_close(lses[r].reshape(-1)[idx], rl, f"shard {r}")
-    ro, rl = oracle.dense(w, rows=rows)
-    assert_o_close(merged.reshape(-1, 512)[idx], ro, "merged")
-    assert_lse_close(mlse.reshape(-1)[idx], rl, "merged")
-
-
-def test_full_size_sparse_dcp_config_sampled():
-    w = W.config_sparse_dcp()
-    d = upload(w)
-    parts, lses = run(d)
-    merged, mlse = md.mla_merge_lse(parts, lses, out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    rows = sampled_rows(w, 24, 7)
-    idx = torch.from_numpy(rows).cuda()
-    for r in (0, 3, 7):
-        ro, rl = oracle.sparse(w, rows=rows, num_shards=8, interleave=64, shard_id=r)
-        assert_o_close(parts[r].reshape(-1, 512)[idx], ro, f"shard {r}")
-        assert_lse_close(lses[r].reshape(-1)[idx], rl, f"shard {r}")
-    ro, rl = oracle.sparse(w, rows=rows)
-    assert_o_close(merged.reshape(-1, 512)[idx], ro, "merged")
-    assert_lse_close(mlse.reshape(-1)[idx], rl, "merged")
-
-
-def test_fp16_partials_keep_bf16_accuracy_at_large_magnitudes():
-    """bf16-output calls store split-KV partials as fp16 with a power-of-two scale
-    per (row, 128-column quarter).  With the cache scaled by 4 (exact in bf16)
-    outputs reach |O| > 4 and every sequence is split into many partitions.
-
-    At this scale the absolute 1e-2 bar does not apply: the bf16 softmax weights
-    (relative step 2^-9 each; O is normalised by their own sum) move O by up to
-    2^-9 * sum_p w_p |v_p - O| <= 2^-8 * max|V|.  So both paths are held to that
-    bound against the oracle, and the fp16-partial path (bf16 out) is held to the
-    fp32-partial path (fp32 out) within the partials' 2^-11 relative step of the
-    largest value a partial can hold (max|V|) plus the final bf16 rounding."""
+def test_fp16_partials_at_magnitudes_beyond_the_contract():
+    """The same path with the cache scaled by 4 (exact in bf16): scores spread
+    4x wider and |O| exceeds 4, outside the N(0,1) inputs the contract bar is
+    stated for.  There, the bf16 rounding of the softmax weights (relative step
+    2^-9 each; O is normalised by their own sum) moves O by up to
+    2^-9 * sum_p w_p |v_p - O| <= 2^-8 max|V|, which the fp32-output path is held
+    to; the fp16-partial path must add no more than its partials' storage step
+    (2^-11 of a quarter row's largest value) and the final bf16 rounding."""
     w = W.make_workload("scaled_cache_b2_h128_s2048", 2, 1, 128, [2048, 1300], 64, seed=41)
     w.kv = f32_to_bf16_bits(bf16_bits_to_f32(w.kv) * np.float32(4.0)).reshape(w.kv.shape)
     d = upload(w)
@@ -570,8 +515,6 @@ def test_fp16_partials_keep_bf16_accuracy_at_large_magnitudes():
     v_max = float(np.nanmax(np.abs(bf16_bits_to_f32(w.kv[..., :512]))))  # spare blocks hold NaN
     g_b = ob.float().cpu().numpy().reshape(ro.shape).astype(np.float64)
     g_f = of.float().cpu().numpy().reshape(ro.shape).astype(np.float64)
-    p_bound = 2.0 ** -8 * v_max + 1e-4
-    assert np.abs(g_f - ro).max() <= p_bound
-    assert np.all(np.abs(g_b - ro) <= p_bound + 2.0 ** -11 * v_max + 0.5 * ulp_bf16(np.abs(ro) * 1.01))
-    agree = 2.0 ** -11 * v_max + 0.5 * ulp_bf16(np.abs(g_f) * 1.001) + 1e-6
-    assert np.all(np.abs(g_b - g_f) <= agree)
+    parity._note("fp16_partials_cache_x4", max_abs_dO=np.abs(g_b - ro).max(), max_abs_O_ref=np.abs(ro).max())
+    assert np.abs(g_f - ro).max() <= 2.0 ** -8 * v_max + 1e-4
+    assert np.all(np.abs(g_b - g_f) <= 2.0 ** -11 * v_max + parity.ulp_bf16(np.abs(g_f) * 1.001) * 0.5 + 1e-6)
