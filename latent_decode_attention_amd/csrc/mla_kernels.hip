@@ -49,6 +49,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+// Register index of each element of a 16-register MFMA result.
+constexpr u32x16 kRegIndex = {0u, 1u, 2u, 3u, 4u, 5u, 6u, 7u, 8u, 9u, 10u, 11u, 12u, 13u, 14u, 15u};
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -73,6 +76,14 @@ constexpr float kKv8Bias = 128.0f;
 // unit is recomputed with a higher reference: p <= 2^60 keeps sum(p) * |v| far
 // inside the fp32 range for any realistic row.
 constexpr float kHeadroomLog2 = 60.0f;
+// Share of a row's weight from which a token's bf16 rounding in P.V is undone
+// at the end (one token's rounding moves O by up to 2^-9 x share x |v - O|) ...
+constexpr float kExactShare = 0.25f;
+// ... in rows whose output reaches this magnitude in the wave's 128 columns.
+// Below it a bf16 output's own rounding (at most 2^-8 there) leaves 0.006 of
+// a 1e-2 budget; the two values were chosen on seeded workloads with RoPE-key
+// outliers, where rows are dominated by a few tokens.
+constexpr float kExactMinOut = 2.0f;
 constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unconstrained
 
 static_assert(kTile == 16 * kWaves, "each wave copies 16 rows of a tile");
@@ -597,6 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // the chain leaves the query loads issued after it in flight.
   TileMask mask_cur;
   int pn1, bn1, pn2;
+  int row_cur = -1;  // 64-row groups: cache row of this lane's token (lane = token) in the current tile
   // int8 cache: the row factor each lane (= token) loaded for the current tile,
   // and whether its token is attended at all (else the factor is taken as 0).
   float sig_raw = 0.f;
@@ -616,6 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     after_blocks();
     __builtin_amdgcn_sched_barrier(0);
     const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
+    if constexpr (kRows == 64) row_cur = row0;
     if constexpr (kKv8) {
       copy_all8(prepare_copy8(sm.tile[0], a, wave, lane, row0), std::make_integer_sequence<int, kCopySteps8>());
       sig_raw = a.kv_scale[max(row0, 0)];
@@ -713,12 +726,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // never rescaled; a score beyond that headroom sends the unit through a
   // recompute pass.
   float m_ref = -INFINITY;
-  float m_seen = -INFINITY;  // largest score seen so far
   float l_run = 0.f;         // this lane's share of sum(p), for lse
   float l_rnd = 0.f;         // the same sum over p as rounded to bf16, for O
   float l_cvx = 0.f;         // int8 cache: sum of the rounded weights over their row factors, for O
   f32x16 acc[kAccTiles];     // acc[4 rt + ct]: rows 32 rt.., columns 128 wave + 32 ct..
   bool first_pass = true;
+  // The lane's largest score of the pass and its token (64-row groups: the
+  // token's cache row; 128-row groups: its index in the unit's stream).
+  // Every score carries its register index in its 4 lowest mantissa bits (a
+  // change of at most 2^-19 of the score), so a maximum also names its token:
+  // the finalize step restores that token's exact weight (see there).
+  float best_x = -INFINITY;
+  int best_row = -1;
 
   for (;;) {
     bf16x8 z = zero8;
@@ -728,6 +747,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     l_run = 0.f;
     l_rnd = 0.f;
     l_cvx = 0.f;
+    best_x = -INFINITY;
+    best_row = -1;
     bool overflow = false;
 
     for (int t = 0; t < ntiles; ++t) {
@@ -844,6 +865,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = sg[r] * (s[r] - q_bias);
         }
+        {
+          // Whole-vector integer ops: per-element updates of a vector
+          // miscompile with this toolchain (every element read element 0).
+          const u32x16 tagged = (__builtin_bit_cast(u32x16, s) & ~15u) | kRegIndex;
+          s = __builtin_bit_cast(f32x16, tagged);
+        }
         if (mask_cur.full) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] = s[r];
@@ -863,8 +890,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         float smax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) smax = fmaxf(smax, x[r]);
+        {
+          // The token of the lane's largest score in this block (register
+          // index from the tag): 64-row groups keep its cache row, fetched
+          // from the lane that holds it; 128-row groups (no register to spare
+          // in the tile loop) its stream index, looked up at the end.
+          const int rb = (int)(__builtin_bit_cast(unsigned, smax) & 15u);
+          const int tok_b = 32 * tok + 8 * (rb >> 2) + 4 * half + (rb & 3);
+          const int id_b = kRows == 128 ? t * kTile + tok_b : __shfl(row_cur, tok_b);
+          if (smax > best_x) {
+            best_x = smax;
+            best_row = id_b;
+          }
+        }
         smax = fmaxf(smax, __shfl_xor(smax, 32)) * a.scale_log2;
-        m_seen = fmaxf(m_seen, smax);
         if constexpr (kRows == 128) {
           if (m_ref == -INFINITY) m_ref = smax;  // first scores of this row: acc is still 0
         } else if (first_pass && t == 0) {
@@ -947,6 +986,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       }
 
       mask_cur = mask1;
+      if constexpr (kRows == 64) row_cur = row1;
       sig_raw = sig1_raw;
       sig_ok = sig1_ok;
       pn1 = pn2;
@@ -963,6 +1003,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     int *vote = reinterpret_cast<int *>(sm.tile[0]);
     float *seen = reinterpret_cast<float *>(sm.tile[0] + 64);
     if (lane == 0) vote[wave] = __any(overflow) ? 1 : 0;
+    // The row's largest score of the pass, base 2 (the scale is positive, so
+    // scaling after the maximum is exact).
+    const float m_seen = fmaxf(best_x, __shfl_xor(best_x, 32)) * a.scale_log2;
     if (kRows == 64 && half == 0) seen[wave * 32 + n] = m_seen;
     __syncthreads();
     const bool redo = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
@@ -986,6 +1029,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     l_sh[wave * 32 + n] = l_run_w;
     l_sh[kWaves * 32 + wave * 32 + n] = l_rnd_w;
     if constexpr (kKv8) l_sh[2 * kWaves * 32 + wave * 32 + n] = l_cvx_w;
+  }
+  // Each lane's candidate for the exact-weight step below: the cache row of
+  // the token of its largest score this pass and that token's weight p
+  // exactly as the softmax step computed it.  [scoring wave][half][row lane].
+  int *cand_row = reinterpret_cast<int *>(sm.tile[0] + 2048);
+  float *cand_p = reinterpret_cast<float *>(sm.tile[0] + 3072);
+  {
+    float cp = 0.f;
+    if (best_x > -INFINITY) {
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      cp = __builtin_amdgcn_exp2f(__builtin_fmaf(best_x, a.scale_log2, -m_use));
+    }
+    cand_row[(wave * 2 + half) * 32 + n] = best_x > -INFINITY ? best_row : -1;
+    cand_p[(wave * 2 + half) * 32 + n] = cp;
   }
   lds_barrier();
   // Row sum of kind k (0: exact, 1: rounded) of row 32 r_t + n.
@@ -1028,14 +1085,139 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // bf16 cache: normalised by the sum of the rounded weights used.  int8
     // cache: the bias times that sum comes off, then division by the sum of
     // those weights over their factors (an exact convex combination again).
-    const float l = row_sum(kKv8 ? 2 : 1, rt);
-    const float c0 = kKv8 ? kKv8Bias * row_sum(1, rt) : 0.f;
-    auto unbias = [&](float x) { return kKv8 ? x - c0 : x; };
     const bool ok = r < u.rows;
     const int64_t gr = ok ? out_row(r) : 0;
-    f32x16 v[4];
+    // This row tile's accumulators as plain floats (the exact-weight step
+    // below adds to them; element writes into vectors miscompile).
+    float ov[4][16];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) v[ct] = acc[4 * rt + ct];
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x16 t = acc[4 * rt + ct];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ov[ct][e] = t[e];
+    }
+    float l_rnd_row = row_sum(1, rt);
+    float l_cvx_row = kKv8 ? row_sum(2, rt) : 0.f;
+    // Exact-weight step.  P.V used every weight rounded to bf16 (relative
+    // error up to 2^-9).  Where a few tokens carry much of a row's weight and
+    // the output is large, that rounding alone moves O by up to 2^-9 |v - O|
+    // per token, more than the output's own precision leaves room for.  The
+    // row's largest-score token is always among the candidates of its scoring
+    // lanes; each candidate holding at least kExactShare of the row's weight,
+    // in a row whose output reaches kExactMinOut in the wave's columns, gets
+    // the rest of its weight back: O += (p - bf16(p)) v, with the normaliser
+    // raised by the same amount (int8 cache: the factor-carrying weight, and
+    // that weight over the factor).  Each wave decides for its own 128 columns
+    // of the row, so every column stays a convex combination of V rows.
+    {
+      constexpr int kCands = kRows == 128 ? 2 : 4;
+      const float l_exact = row_sum(0, rt);
+      const float l0 = kKv8 ? l_cvx_row : l_rnd_row;
+      const float c00 = kKv8 ? kKv8Bias * l_rnd_row : 0.f;
+      float omax = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) omax = fmaxf(omax, fabsf(ov[ct][e] - c00));
+      // Decided for the row's 128 columns of this wave, by both lanes that hold
+      // them: they share one normaliser (and, for fp16 partials, one scale).
+      omax = fmaxf(omax, __shfl_xor(omax, 32));
+      const bool big = omax >= kExactMinOut * l0 && l0 > 0.f;
+      int crow[kCands];
+      float cp[kCands];
+      bool need[kCands];
+      bool any = false;
+#pragma unroll
+      for (int k = 0; k < kCands; ++k) {
+        const int src = ((rt + 2 * (k >> 1)) * 2 + (k & 1)) * 32 + n;
+        crow[k] = cand_row[src];
+        cp[k] = cand_p[src];
+        need[k] = big && crow[k] >= 0 && cp[k] >= kExactShare * l_exact;
+        any |= need[k];
+      }
+      if (__any(any)) {
+        // Candidates in batches whose loads are all issued before any is used
+        // (the 64-row kernels take all four at once; the 128-row kernels,
+        // whose tile loop uses every register, one at a time), each loaded
+        // word split into scalars at once; rows a lane does not need are not read.
+        constexpr int kBatch = kRows == 128 ? 1 : kCands;
+        constexpr int kWords = kKv8 ? 16 : 32;
+        const int col0 = 128 * wave + 4 * half;
+#pragma unroll
+        for (int k0 = 0; k0 < kCands; k0 += kBatch) {
+          int rowk[kBatch];
+          if constexpr (kRows == 128) {
+            // 128-row groups keep the stream index: position, block, row.
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+              const int pos = need[k0 + k] ? raw_position<kMode>(a, u, u.i0 + crow[k0 + k]) : 0;
+              const int blk = need[k0 + k] ? raw_block(a, u, pos) : 0;
+              rowk[k] = blk * a.block_size + (pos & (a.block_size - 1));
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) rowk[k] = crow[k0 + k];
+          }
+          unsigned raw[kBatch][kWords];
+          float fac[kBatch];
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            fac[k] = 1.f;
+#pragma unroll
+            for (int m = 0; m < kWords; ++m) raw[k][m] = 0u;
+            if (need[k0 + k]) {
+              if constexpr (kKv8) {
+                fac[k] = a.kv_scale[rowk[k]];
+                const char *code = reinterpret_cast<const char *>(a.kv) + (int64_t)rowk[k] * kRowBytes8 + col0;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                  raw[k][m] = *reinterpret_cast<const unsigned *>(code + 32 * (m >> 2) + 8 * (m & 3));
+              } else {
+                const char *vrow = reinterpret_cast<const char *>(a.kv) + (int64_t)rowk[k] * kRowBytes + 2 * col0;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                  const u32x2 w2 = *reinterpret_cast<const u32x2 *>(vrow + 2 * (32 * (m >> 2) + 8 * (m & 3)));
+                  raw[k][2 * m] = w2[0];
+                  raw[k][2 * m + 1] = w2[1];
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            if (!need[k0 + k]) continue;
+            const float pk = cp[k0 + k];
+            if constexpr (kKv8) {
+              const float fs = fac[k] != 0.f ? fac[k] : 0x1p-100f;
+              const float pw = pk * fs;
+              const float d = pw - __builtin_bit_cast(float, pack_bf16(pw, 0.f) << 16);
+#pragma unroll
+              for (int m = 0; m < 16; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  ov[m >> 2][4 * (m & 3) + j] += d * (float)(((raw[k][m] >> (8 * j)) & 255u) ^ 128u);
+              l_rnd_row += d;
+              l_cvx_row += d * (1.f / fs);
+            } else {
+              const float d = pk - __builtin_bit_cast(float, pack_bf16(pk, 0.f) << 16);
+#pragma unroll
+              for (int m = 0; m < 16; ++m) {
+                const unsigned lo = raw[k][2 * m], hi = raw[k][2 * m + 1];
+                float *dst = &ov[m >> 2][4 * (m & 3)];
+                dst[0] += d * __builtin_bit_cast(float, lo << 16);
+                dst[1] += d * __builtin_bit_cast(float, lo & 0xFFFF0000u);
+                dst[2] += d * __builtin_bit_cast(float, hi << 16);
+                dst[3] += d * __builtin_bit_cast(float, hi & 0xFFFF0000u);
+              }
+              l_rnd_row += d;
+            }
+          }
+        }
+      }
+    }
+    const float l = kKv8 ? l_cvx_row : l_rnd_row;
+    const float c0 = kKv8 ? kKv8Bias * l_rnd_row : 0.f;
+    auto unbias = [&](float x) { return kKv8 ? x - c0 : x; };
     float mult = l > 0.f ? 1.f / l : 0.f;
     if (okind == kOutFp16) {
       // Scale this row's 128 columns (the two lanes of the row hold them all)
@@ -1044,7 +1226,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(unbias(v[ct][e])));
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(unbias(ov[ct][e])));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       float inv_scale;
       mult *= fp16_scale(mx * mult, &inv_scale);
@@ -1056,8 +1238,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 o = {unbias(v[ct][4 * i]) * mult, unbias(v[ct][4 * i + 1]) * mult,
-                         unbias(v[ct][4 * i + 2]) * mult, unbias(v[ct][4 * i + 3]) * mult};
+        const f32x4 o = {unbias(ov[ct][4 * i]) * mult, unbias(ov[ct][4 * i + 1]) * mult,
+                         unbias(ov[ct][4 * i + 2]) * mult, unbias(ov[ct][4 * i + 3]) * mult};
         const int col = 32 * ct + 8 * i + 4 * half;
         if (wide_out) {
           *reinterpret_cast<f32x4 *>(stage + n * pitch + col * 4) = o;
