@@ -57,8 +57,10 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (e.g. d_qk != 576) */
   MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < mla_workspace_size(...) */
   MLA_ERR_LAUNCH = 5,              /* the HIP runtime rejected a kernel launch */
-  MLA_ERR_DEVICE = 6               /* the current HIP device is missing or not a gfx950 (checked
+  MLA_ERR_DEVICE = 6,              /* the current HIP device is missing or not a gfx950 (checked
                                       on the host once per device, before any launch) */
+  MLA_ERR_SCRATCH_LIMIT = 7        /* mla_decode_sparse_noalloc: the call needs more scratch than
+                                      the library's fixed buffer (MLA_NOALLOC_SCRATCH_BYTES) */
 } mla_status_t;
 
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
@@ -177,6 +179,26 @@ mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indi
                                int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
                                void *out, mla_dtype_t out_dtype, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * mla_decode_sparse without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops, harnesses
+ * that forbid allocation).  Arguments, results and status codes as
+ * mla_decode_sparse.  The call allocates nothing: the split-KV partial results
+ * go to a fixed device buffer of MLA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each device it runs on until the process ends (its address is
+ * looked up once per device).  A call whose plan needs more scratch than that
+ * (mla_workspace_size(problem, 1, 1, -1, top_k, index_stride_q) is the amount)
+ * returns MLA_ERR_SCRATCH_LIMIT and enqueues nothing.  Every call on a device
+ * shares that device's buffer: calls that overlap on one device (on different
+ * streams, or from several host threads) race and must be serialised by the
+ * caller; calls on one stream run in order.  Nothing in the buffer needs to
+ * start at zero.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status_t mla_decode_sparse_noalloc(const mla_problem_t *problem, const int32_t *indices,
+                                       int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
+                                       void *out, mla_dtype_t out_dtype, float *lse, void *stream);
 
 /*
  * Sparse decode under decode context parallelism: the index list of each

@@ -25,6 +25,7 @@ namespace {
 using namespace mla;
 
 constexpr int kDefaultCus = 256;  // MI355X
+static_assert(MLA_NOALLOC_SCRATCH_BYTES == kScratchBytes, "the header states the scratch size");
 constexpr int kMaxShards = 4096;
 constexpr int kMaxTopK = 65536;
 constexpr int kMaxMergeParts = 1024;
@@ -387,6 +388,27 @@ mla_status_t mla_decode_sparse(const mla_problem_t *problem, const int32_t *indi
              out_dtype == MLA_DTYPE_FP32, lse, workspace, workspace_bytes, stream);
 }
 
+mla_status_t mla_decode_sparse_noalloc(const mla_problem_t *problem, const int32_t *indices,
+                                       int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
+                                       void *out, mla_dtype_t out_dtype, float *lse, void *stream) {
+  mla_status_t st = check_problem(problem);
+  if (st != MLA_OK) return st;
+  if (!indices || !out || !lse) return MLA_ERR_NULL_POINTER;
+  if (out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_FP32) return MLA_ERR_BAD_SHAPE;
+  if (top_k < 1 || index_stride_b < 0 || index_stride_q < 0) return MLA_ERR_BAD_SHAPE;
+  Plan pl;
+  st = make_plan(problem, 1, 1, -1, top_k, index_stride_q, device_cus(), &pl);
+  if (st != MLA_OK) return st;
+  if (pl.ws_total > kScratchBytes) return MLA_ERR_SCRATCH_LIMIT;
+  DeviceState *dev;
+  if (current_device(&dev) != MLA_OK) return MLA_ERR_DEVICE;
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  if (pl.ws_total > 0 && scratch_buffer(&ws, &ws_bytes) != hipSuccess) return MLA_ERR_DEVICE;
+  return run(problem, pl, true, indices, top_k, index_stride_b, index_stride_q, 1, 1, -1, out,
+             out_dtype == MLA_DTYPE_FP32, lse, ws, ws_bytes, stream);
+}
+
 mla_status_t mla_decode_sparse_dcp(const mla_problem_t *problem, const int32_t *indices,
                                    int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,
                                    int32_t num_shards, int32_t interleave, int32_t shard_id,
@@ -488,7 +510,9 @@ const char *mla_status_string(mla_status_t s) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: valid arguments this library does not implement";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < mla_workspace_size()";
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
-    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable gfx950 device";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: the current HIP device is missing or not a gfx950";
+    case MLA_ERR_SCRATCH_LIMIT:
+      return "MLA_ERR_SCRATCH_LIMIT: the call needs more scratch than the library's fixed 64 MiB buffer";
   }
   return "unknown mla_status_t";
 }

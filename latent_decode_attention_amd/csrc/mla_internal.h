@@ -118,4 +118,11 @@ hipError_t launch_topk(const TopkArgs &args, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs &args, hipStream_t stream);
 
+// Device scratch for the entry point that allocates nothing: a fixed array in
+// device memory (one per device, for the life of the process).  On success
+// *ptr is its device address on the current device (looked up once per
+// device) and *bytes its size.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_buffer(void **ptr, size_t *bytes);
+
 }  // namespace mla

@@ -33,10 +33,18 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
 #include "mla_internal.h"
+
+// Scratch of the decode entry point that allocates nothing (for callers that
+// cannot allocate device memory).  Every device the library runs on holds its
+// own copy until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device (the name itself
+// is a host-side stand-in, not a device address).
+static __device__ __align__(256) char scratch[mla::kScratchBytes];
 
 namespace mla {
 namespace {
@@ -1908,6 +1916,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
 }
 
 }  // namespace
+
+hipError_t scratch_buffer(void **ptr, size_t *bytes) {
+  // The address of each device's copy, looked up the first time a call runs
+  // on that device (with it current), then reused.
+  constexpr int kMaxDevices = 64;
+  static void *addr[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(kThreads);

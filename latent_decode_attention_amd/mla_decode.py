@@ -23,7 +23,7 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE",
                 3: "MLA_ERR_UNSUPPORTED", 4: "MLA_ERR_WORKSPACE_TOO_SMALL", 5: "MLA_ERR_LAUNCH",
-                6: "MLA_ERR_DEVICE"}
+                6: "MLA_ERR_DEVICE", 7: "MLA_ERR_SCRATCH_LIMIT"}
 
 
 class MlaError(RuntimeError):
@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_merge_lse.restype = ctypes.c_int
     lib.mla_kv_write.argtypes = [vp, vp, i64, vp, i64, vp, i32, i32, i32, vp]
     lib.mla_kv_write.restype = ctypes.c_int
+    lib.mla_decode_sparse_noalloc.argtypes = [P, vp, i32, i64, i64, vp, i32, vp, vp]
+    lib.mla_decode_sparse_noalloc.restype = ctypes.c_int
     lib.mla_decode_sparse_dcp.argtypes = [P, vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.mla_decode_sparse_dcp.restype = ctypes.c_int
     lib.mla_topk_select.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, vp, vp]
@@ -241,6 +243,31 @@ def mla_decode_sparse(q, kv, block_table, seq_lens, indices, *, scale: float, ma
     _check(lib.mla_decode_sparse(ctypes.byref(p), _ptr(indices), top_k, index_stride_b, index_stride_q,
                                  _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
                                  0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_sparse_noalloc(q, kv, block_table, seq_lens, indices, *, scale: float, max_seq_len: int,
+                              top_k: Optional[int] = None, index_stride_b: Optional[int] = None,
+                              index_stride_q: Optional[int] = None, out: torch.Tensor, lse: torch.Tensor,
+                              stream=None, kv_scale: Optional[torch.Tensor] = None):
+    """mla_decode_sparse into caller-given out [B,Q,h_q,512] (bf16 or fp32) and lse [B,Q,h_q]
+    fp32, with the library's fixed device scratch instead of a workspace: allocates nothing."""
+    p = make_problem(q, kv, block_table, seq_lens, scale, max_seq_len, kv_scale)
+    if indices.dtype != torch.int32 or not indices.is_contiguous() or not indices.is_cuda:
+        raise TypeError("indices must be a contiguous int32 GPU tensor")
+    B, Q, h_q, _ = q.shape
+    if top_k is None:
+        top_k = indices.shape[-1]
+    if index_stride_q is None:
+        index_stride_q = top_k if indices.dim() == 3 else 0
+    if index_stride_b is None:
+        index_stride_b = (indices.shape[1] * top_k) if indices.dim() == 3 else top_k
+    if indices.numel() < (B - 1) * index_stride_b + (Q - 1) * index_stride_q + top_k:
+        raise TypeError("indices is smaller than its strides imply")
+    if tuple(out.shape) != (B, Q, h_q, 512) or tuple(lse.shape) != (B, Q, h_q) or lse.dtype != torch.float32:
+        raise TypeError("out/lse have the wrong shape or dtype")
+    _check(lib.mla_decode_sparse_noalloc(ctypes.byref(p), _ptr(indices), top_k, index_stride_b, index_stride_q,
+                                         _ptr(out), _dtype_code(out.dtype), _ptr(lse), _stream(stream)))
     return out, lse
 
 

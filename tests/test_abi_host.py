@@ -314,3 +314,21 @@ def test_valid_calls_without_a_device_return_mla_err_device():
     assert lib.mla_merge_lse(FAKE, FAKE, 2, 4, 512, FAKE, 1, FAKE, None) == 6
     assert lib.mla_topk_select(FAKE, 4096, 2048, FAKE, 2, 2, 2048, 64, FAKE, None) == 6
     assert lib.mla_kv_write(FAKE, FAKE, 10, FAKE, 100, FAKE, 1, 1, 0, None) == 6
+
+
+def test_noalloc_entry_point_checks_arguments_and_its_scratch_limit():
+    """The allocation-free sparse call validates like mla_decode_sparse and
+    rejects, before touching the device, a plan needing more than its fixed
+    buffer (mla_workspace_size gives the amount)."""
+    f = lib.mla_decode_sparse_noalloc
+    p = problem()
+    assert f(ctypes.byref(p), None, 2048, 2048, 0, FAKE, 0, FAKE, None) == 1
+    assert f(ctypes.byref(p), FAKE, 0, 2048, 0, FAKE, 0, FAKE, None) == 2
+    assert f(ctypes.byref(p), FAKE, 2048, -1, 0, FAKE, 0, FAKE, None) == 2
+    assert f(ctypes.byref(p), FAKE, 2048, 2048, 0, FAKE, 7, FAKE, None) == 2
+    assert f(ctypes.byref(problem(d_qk=512)), FAKE, 2048, 2048, 0, FAKE, 0, FAKE, None) == 3
+    big = problem(B=8, Q=4, h_q=128, max_seq_len=65536, max_blocks=1024, num_blocks=16384)
+    need = md.mla_workspace_size(big, 1, 1, -1, 4096, 0)
+    assert need > (64 << 20)
+    assert f(ctypes.byref(big), FAKE, 4096, 4096, 0, FAKE, 0, FAKE, None) == 7
+    assert "64 MiB" in md.mla_status_string(7)
