@@ -311,8 +311,11 @@ __device__ __forceinline__ TileMask tile_mask(const DecodeArgs &a, const Unit &u
   unsigned long long all = ~0ull;
 #pragma unroll
   for (int qq = 0; qq < kMaxQPerGroup; ++qq) {
-    t.m[qq] = qq < a.q_per_group ? __ballot(row >= 0 && p <= u.S - a.Q + u.q0 + qq) : 0ull;
-    if (qq < a.q_per_group) all &= t.m[qq];
+    // Query tokens past the group's own attend nothing: a limit of -1,
+    // chosen on the scalar unit rather than by branching around the ballot.
+    const int lim = qq < a.q_per_group ? u.S - a.Q + u.q0 + qq : -1;
+    t.m[qq] = __ballot(row >= 0 && p <= lim);
+    all &= qq < a.q_per_group ? t.m[qq] : ~0ull;
   }
   t.full = all == ~0ull;
   return t;
@@ -1106,6 +1109,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     }
     float l_rnd_row = row_sum(1, rt);
     float l_cvx_row = kKv8 ? row_sum(2, rt) : 0.f;
+    // Largest magnitude of the row's unnormalised outputs in this lane's
+    // columns (the exact-weight gate below and the fp16 partial scale).
+    float omax = 0.f;
+    {
+      const float cb = kKv8 ? kKv8Bias * l_rnd_row : 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) omax = fmaxf(omax, fabsf(ov[ct][e] - cb));
+    }
+    float omax_fixed = omax;  // before the step's corrections (which add under 2^-9 of a weight)
     // Exact-weight step.  P.V used every weight rounded to bf16 (relative
     // error up to 2^-9).  Where a few tokens carry much of a row's weight and
     // the output is large, that rounding alone moves O by up to 2^-9 |v - O|
@@ -1121,12 +1135,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       constexpr int kCands = kRows == 128 ? 2 : 4;
       const float l_exact = row_sum(0, rt);
       const float l0 = kKv8 ? l_cvx_row : l_rnd_row;
-      const float c00 = kKv8 ? kKv8Bias * l_rnd_row : 0.f;
-      float omax = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) omax = fmaxf(omax, fabsf(ov[ct][e] - c00));
       // Decided for the row's 128 columns of this wave, by both lanes that hold
       // them: they share one normaliser (and, for fp16 partials, one scale).
       omax = fmaxf(omax, __shfl_xor(omax, 32));
@@ -1144,6 +1152,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         any |= need[k];
       }
       if (__any(any)) {
+        omax_fixed = -1.f;  // recomputed after the corrections
         // Candidates in batches whose loads are all issued before any is used
         // (the 64-row kernels take all four at once; the 128-row kernels,
         // whose tile loop uses every register, one at a time), each loaded
@@ -1230,11 +1239,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if (okind == kOutFp16) {
       // Scale this row's 128 columns (the two lanes of the row hold them all)
       // so their largest magnitude uses fp16's full range.
-      float mx = 0.f;
+      float mx = omax_fixed;
+      if (mx < 0.f) {
+        mx = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(unbias(ov[ct][e])));
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(unbias(ov[ct][e])));
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       float inv_scale;
       mult *= fp16_scale(mx * mult, &inv_scale);
