@@ -510,8 +510,7 @@ def main():
                      "frac": (achieved_gbs / HBM_PEAK_GBS) if bound == "hbm" else
                              (achieved_tfs / MFMA_BF16_PEAK_TFS),
                      "traffic": traffic,
-                     "kernel": (("partition_kernel+" if sharded and w.indices is not None else "") +
-                                "decode_kernel" + ("+merge_kernel" if splits > 1 or sharded else "")),
+                     "kernel": "decode_kernel" + ("+merge_kernel" if splits > 1 or sharded else ""),
                      "launch_ms": call_ms,
                      "mfma_tflops": achieved_tfs,
                      "mfma_frac": achieved_tfs / MFMA_BF16_PEAK_TFS,

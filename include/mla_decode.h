@@ -219,10 +219,10 @@ mla_status_t mla_decode_sparse_noalloc(const mla_problem_t *problem, const int32
  *              index_stride_q) bytes (never 0: it holds each shard's part of
  *              every list).
  *
- * The call first splits every list by owner shard (in list order) into the
- * workspace, then each shard streams only its own part; partitions are cut for
- * an even share, min(top_k, max_seq_len) / num_shards entries, so lists that
- * crowd one shard stay correct but run longer.
+ * Each work-group first picks its shard's entries of its list (in list order)
+ * into the workspace, then streams only those; partitions are cut for an even
+ * share, min(top_k, max_seq_len) / num_shards entries, so lists that crowd one
+ * shard stay correct but run longer.
  */
 mla_status_t mla_decode_sparse_dcp(const mla_problem_t *problem, const int32_t *indices,
                                    int32_t top_k, int64_t index_stride_b, int64_t index_stride_q,

@@ -35,8 +35,7 @@ struct Plan {
   int kernel_rows;  // 128 or 64
   int units, splits, chunk, stream_len;
   int64_t grid;
-  int lists_q;  // sparse under DCP: per-shard lists kept per query token (Q) or shared (1)
-  size_t ws_o, ws_lse, ws_scale, ws_lists, ws_counts, ws_total;
+  size_t ws_o, ws_lse, ws_scale, ws_lists, ws_total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -84,9 +83,9 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   if (num_cus < 1) num_cus = kDefaultCus;
   int64_t L;
   if (sparse && num_shards > 1) {
-    // Each shard streams its own part of the list (split off by
-    // partition_kernel); partitions are cut for an even share, and the last
-    // partition of a unit takes whatever a skewed list adds beyond it.
+    // Each shard streams its own part of the list (picked out by the decode
+    // work-groups themselves); partitions are cut for an even share, and the
+    // last partition of a unit takes whatever a skewed list adds beyond it.
     const int64_t valid = std::min<int64_t>(top_k, p->max_seq_len);
     L = (valid + num_shards - 1) / num_shards;
   } else if (sparse) {
@@ -182,15 +181,13 @@ mla_status_t make_plan(const mla_problem_t *p, int num_shards, int interleave, i
   } else {
     pl->ws_o = pl->ws_lse = pl->ws_scale = 0;
   }
-  pl->lists_q = shared_list ? 1 : p->Q;
-  pl->ws_lists = pl->ws_counts = 0;
+  pl->ws_lists = 0;
   if (sparse && num_shards > 1) {
-    // Sized for one list per query token so that one size fits either layout.
-    const int64_t lists = (int64_t)p->B * p->Q * pl->shard_units;
-    pl->ws_lists = align256((size_t)(lists * top_k) * sizeof(int32_t));
-    pl->ws_counts = align256((size_t)lists * sizeof(int32_t));
+    // Each unit's shard entries, top_k slots per unit (its partitions fill
+    // disjoint ranges of them).
+    pl->ws_lists = align256((size_t)((int64_t)pl->units * top_k) * sizeof(int32_t));
   }
-  pl->ws_total = pl->ws_o + pl->ws_lse + pl->ws_scale + pl->ws_lists + pl->ws_counts;
+  pl->ws_total = pl->ws_o + pl->ws_lse + pl->ws_scale + pl->ws_lists;
   return MLA_OK;
 }
 
@@ -298,27 +295,9 @@ mla_status_t run(const mla_problem_t *p, const Plan &pl, bool sparse, const int3
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (sparse && num_shards > 1) {
-    char *ws = static_cast<char *>(workspace) + pl.ws_o + pl.ws_lse + pl.ws_scale;
-    PartitionArgs pa;
-    pa.indices = indices;
-    pa.stride_b = stride_b;
-    pa.stride_q = stride_q;
-    pa.seq_lens = p->seq_lens;
-    pa.top_k = top_k;
-    pa.B = p->B;
-    pa.lists_q = pl.lists_q;
-    pa.num_shards = num_shards;
-    pa.interleave = interleave;
-    pa.by_interleave = make_fastdiv((uint32_t)interleave);
-    pa.by_shards = make_fastdiv((uint32_t)num_shards);
-    pa.shard_base = a.shard_base;
-    pa.shard_units = pl.shard_units;
-    pa.lists = reinterpret_cast<int32_t *>(ws);
-    pa.counts = reinterpret_cast<int32_t *>(ws + pl.ws_lists);
-    if (launch_partition(pa, s) != hipSuccess) return MLA_ERR_LAUNCH;
-    a.indices = pa.lists;
-    a.idx_counts = pa.counts;
-    a.lists_q = pl.lists_q;
+    a.own_lists = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + pl.ws_o + pl.ws_lse + pl.ws_scale);
+    a.by_interleave = make_fastdiv((uint32_t)interleave);
+    a.by_shards = make_fastdiv((uint32_t)num_shards);
   }
   if (launch_decode(a, pl.grid, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.splits > 1) {

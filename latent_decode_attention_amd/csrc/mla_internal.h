@@ -27,11 +27,13 @@ struct DecodeArgs {
   const int32_t *indices;      // sparse only
   int64_t idx_stride_b, idx_stride_q;
   int32_t top_k;
-  // Sparse under DCP: `indices` holds one list per (sequence, list, shard) of
-  // just that shard's entries ([B, lists_q, shard_units, top_k]) and
-  // idx_counts [B, lists_q, shard_units] their lengths; null otherwise.
-  const int32_t *idx_counts;
-  int32_t lists_q;             // 1 when the query tokens share one list, else Q
+  // Sparse under DCP (own_lists non-null): each work-group picks its shard's
+  // valid entries out of its unit's list, in list order, and keeps the ones
+  // of its partition at own_lists[unit * top_k + i] (i = the entry's rank among
+  // the shard's); by_interleave and by_shards divide a position into its
+  // shard.  Null otherwise.
+  int32_t *own_lists;
+  FastDiv by_interleave, by_shards;
   int32_t sparse;
   int32_t B, Q, h_q;
   int32_t block_size, bs_shift, max_blocks, num_blocks;
@@ -83,22 +85,6 @@ struct KvWriteArgs {
   int32_t num_shards, interleave, shard_id;
 };
 
-// Splitting top-k lists by DCP shard: list (b, l) is
-// indices[b * stride_b + l * stride_q + 0 .. top_k); the entries shard r owns
-// (p >= 0, p < seq_lens[b], floor(p / interleave) mod num_shards = r) are
-// copied in list order to lists[((b * lists_q + l) * shard_units + r -
-// shard_base) * top_k + ...] and their number to counts[...].
-struct PartitionArgs {
-  const int32_t *indices;
-  int64_t stride_b, stride_q;
-  const int32_t *seq_lens;
-  int32_t top_k, B, lists_q;
-  int32_t num_shards, interleave, shard_base, shard_units;
-  FastDiv by_interleave, by_shards;
-  int32_t *lists;
-  int32_t *counts;
-};
-
 // Top-k selection over indexer scores: row (b, q) holds the scores of positions
 // [0, L) with L = clamp(seq_lens[b] - Q + q + 1, 0, max_len) at
 // scores[b * stride_b + q * stride_q + p]; out [B, Q, top_k] receives the
@@ -113,7 +99,6 @@ struct TopkArgs {
 
 // Enqueue the kernels; return the HIP status of the launch.
 hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t stream);
-hipError_t launch_partition(const PartitionArgs &args, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &args, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &args, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs &args, hipStream_t stream);

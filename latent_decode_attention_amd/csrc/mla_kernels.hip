@@ -197,11 +197,13 @@ enum StreamMode { kDenseStream = 0, kShardStream = 1, kSparseStream = 2 };
 
 struct Unit {
   int b, q0, shard, split;
+  int unit;       // (sequence, query group, shard) index: work-group id / splits
   int h0, rows;   // first head and number of query rows of the group
   int64_t row0;   // flattened (query token, head) row of the group's row 0
   int S, i0, i1;
   int64_t idx_base;
-  const int32_t *bt;  // this sequence's block-table row
+  const int32_t *list;  // sparse: the list the stream indexes (idx_base on)
+  const int32_t *bt;    // this sequence's block-table row
 };
 
 // Values the compiler cannot prove wave-uniform (loads from memory the kernel
@@ -215,8 +217,64 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Sparse under DCP: the entries of the unit's list that belong to `shard`
+// (valid positions p, 0 <= p < S, with floor(p / interleave) mod num_shards =
+// shard), in list order ("RFC: MsModeling 支持 Decode Context Parallel 仿真",
+// §2.1.4.1, interleaved placement).  Returns their number L; those of ranks
+// [i0, i1) (i1 = L for the unit's last partition, else min(L, i0 + chunk)),
+// this partition's share, are stored at dst[rank].  Every thread of the
+// work-group takes part: wave w scans a quarter of the list, counting, then
+// again placing its entries after the earlier quarters' counts.  `cnt` is LDS
+// scratch of kWaves ints.
+constexpr int kSelectBatch = 8;  // 64-entry rounds per batch of loads (a whole 2048-entry list)
+__device__ __forceinline__ int select_shard_entries(const DecodeArgs &a, const int32_t *src, int S, unsigned shard,
+                                                    int i0, int chunk, bool last, int32_t *dst, int *cnt) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int quarter = (a.top_k + kWaves * 64 - 1) / (kWaves * 64) * 64;
+  const int lo = wave * quarter, hi = min(a.top_k, lo + quarter);
+  auto owned = [&](int i, int p) {
+    const unsigned run = fastdiv((unsigned)p, a.by_interleave);
+    const unsigned owner = run - fastdiv(run, a.by_shards) * (unsigned)a.num_shards;
+    return i < hi && p >= 0 && p < S && owner == shard;
+  };
+  // Each batch issues all its loads (clamped addresses) before the first use.
+  auto scan = [&](auto visit) {
+    for (int b0 = lo; b0 < hi; b0 += 64 * kSelectBatch) {
+      int v[kSelectBatch];
+#pragma unroll
+      for (int j = 0; j < kSelectBatch; ++j) v[j] = src[min(b0 + 64 * j + lane, a.top_k - 1)];
+#pragma unroll
+      for (int j = 0; j < kSelectBatch; ++j) visit(owned(b0 + 64 * j + lane, v[j]), v[j]);
+    }
+  };
+  int count = 0;
+  scan([&](bool m, int) { count += __popcll(__ballot(m)); });
+  if (lane == 0) cnt[wave] = count;
+  __syncthreads();
+  int rank = 0, L = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = cnt[w];
+    rank += w < wave ? c : 0;
+    L += c;
+  }
+  const int i1 = last ? L : min(L, i0 + chunk);
+  scan([&](bool m, int p) {
+    const unsigned long long bm = __ballot(m);
+    const int r = rank + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((unsigned)bm, 0u));
+    if (m && r >= i0 && r < i1) dst[r] = p;
+    rank += __popcll(bm);
+  });
+  // The stored entries are read back by other waves of the work-group.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return L;
+}
+
 template <int kMode>
-__device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
+__device__ __forceinline__ Unit decode_unit(const DecodeArgs &a, int *lds_scratch) {
   const uint32_t grid = gridDim.x;  // < 2^31 (the plan checks)
   uint32_t id = blockIdx.x;
   // Work-groups are dealt round-robin to the 8 XCDs; renumber so that the
@@ -228,6 +286,7 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
   const uint32_t splits = a.splits, q_groups = a.q_groups, shard_units = a.shard_units, head_chunks = a.head_chunks;
   u.split = (int)(id % splits);
   id /= splits;
+  u.unit = (int)id;
   const uint32_t qg = id % q_groups;
   id /= q_groups;
   const int su = (int)(id % shard_units);
@@ -251,16 +310,20 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
   u.idx_base = 0;
   bool rest = false;  // the last partition also takes what the plan did not foresee
   if constexpr (kMode == kSparseStream) {
-    if (a.idx_counts) {
-      // This shard's own list; its length is known only on the device.  The
-      // plan cuts partitions for an even share of the entries per shard.
-      const int64_t list = ((int64_t)u.b * a.lists_q + (a.lists_q > 1 ? u.q0 : 0)) * a.shard_units + su;
-      L = uniform(a.idx_counts[list]);
-      u.idx_base = uniform(list * a.top_k);
+    const int64_t src = uniform((int64_t)u.b * a.idx_stride_b + (int64_t)u.q0 * a.idx_stride_q);
+    if (a.own_lists) {
+      // This shard's entries of the list; their number is known only on the
+      // device.  The plan cuts partitions for an even share of the entries
+      // per shard, and the last partition takes whatever is beyond.
       rest = u.split == a.splits - 1;
+      u.idx_base = uniform((int64_t)u.unit * a.top_k);
+      u.list = a.own_lists;
+      L = uniform(select_shard_entries(a, a.indices + src, u.S, (unsigned)u.shard, u.split * a.chunk, a.chunk, rest,
+                                       a.own_lists + u.idx_base, lds_scratch));
     } else {
       L = a.top_k;
-      u.idx_base = uniform((int64_t)u.b * a.idx_stride_b + (int64_t)u.q0 * a.idx_stride_q);
+      u.idx_base = src;
+      u.list = a.indices;
     }
   } else if constexpr (kMode == kShardStream) {
     L = shard_len(u.S, a.num_shards, a.interleave, u.shard);
@@ -282,7 +345,7 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs &a) {
 // position the shard owns; sparse: the raw list entry, validated later).
 template <int kMode>
 __device__ __forceinline__ int raw_position(const DecodeArgs &a, const Unit &u, int i) {
-  if constexpr (kMode == kSparseStream) return a.indices[u.idx_base + min(i, u.i1 - 1)];
+  if constexpr (kMode == kSparseStream) return u.list[u.idx_base + min(i, u.i1 - 1)];
   if constexpr (kMode == kShardStream)
     return ((i / a.interleave) * a.num_shards + u.shard) * a.interleave + (i % a.interleave);
   return i;
@@ -293,7 +356,7 @@ __device__ __forceinline__ int raw_block(const DecodeArgs &a, const Unit &u, int
 }
 // Physical cache row of a token, or -1 when no query row of this group attends
 // it.  (Under DCP, streams hold only positions of their own shard: dense
-// streams by construction, sparse ones after partition_kernel.)
+// streams by construction, sparse ones by select_shard_entries.)
 __device__ __forceinline__ int token_row(const DecodeArgs &a, const Unit &u, int i, int p, int blk) {
   const int last = u.S - a.Q + u.q0 + a.q_per_group - 1;
   const bool ok = i < u.i1 && p >= 0 && p <= last && (p >> a.bs_shift) < a.max_blocks && blk >= 0 &&
@@ -559,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int rh = kRows == 128 ? wave : (wave & 1);  // the wave's row tile for the scores
   const int th = kRows == 128 ? 0 : (wave >> 1);    // its token half (64 rows)
 
-  const Unit u = decode_unit<kMode>(a);
+  const Unit u = decode_unit<kMode>(a, reinterpret_cast<int *>(sm.tile[1]));
   const int ntiles = u.i1 > u.i0 ? (u.i1 - u.i0 + kTile - 1) / kTile : 0;
 
   // Output destination: final tensor or this partition's slot of the partials.
@@ -1543,45 +1606,6 @@ __global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWrite
 }
 
 
-// Splitting top-k lists by DCP shard ("RFC: MsModeling 支持 Decode Context
-// Parallel 仿真", §2.1.4.1: position p lives on shard floor(p / I) mod N).  One
-// wave per (sequence, list, shard) scans the list in order and appends the
-// entries its shard owns, so every shard's list keeps the list's order and the
-// result does not depend on scheduling.  Negative entries (padding) and entries
-// at or past the sequence length are dropped here: no query token attends them.
-constexpr int kPartitionThreads = 256;
-constexpr int kPartitionBatch = 32;  // entries per lane per pass: 2048 entries in one round trip
-__global__ __launch_bounds__(kPartitionThreads) void partition_kernel(const PartitionArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t id = (int64_t)blockIdx.x * (kPartitionThreads / 64) + (threadIdx.x >> 6);
-  if (id >= (int64_t)a.B * a.lists_q * a.shard_units) return;  // whole waves leave
-  const int64_t bl = id / a.shard_units;
-  const int l = (int)(bl % a.lists_q), b = (int)(bl / a.lists_q);
-  const unsigned r = (unsigned)(a.shard_base + (int)(id % a.shard_units));
-  const int32_t *src = a.indices + (int64_t)b * a.stride_b + (int64_t)l * a.stride_q;
-  int32_t *dst = a.lists + id * a.top_k;
-  const int S = a.seq_lens[b];
-  int count = 0;
-  for (int base = 0; base < a.top_k; base += 64 * kPartitionBatch) {
-    int v[kPartitionBatch];
-#pragma unroll
-    for (int j = 0; j < kPartitionBatch; ++j)  // every load issued before the first use
-      v[j] = src[min(base + 64 * j + lane, a.top_k - 1)];
-#pragma unroll
-    for (int j = 0; j < kPartitionBatch; ++j) {
-      const int p = v[j];
-      const unsigned run = fastdiv((unsigned)p, a.by_interleave);
-      const unsigned owner = run - fastdiv(run, a.by_shards) * (unsigned)a.num_shards;
-      const bool mine = base + 64 * j + lane < a.top_k && p >= 0 && p < S && owner == r;
-      const unsigned long long m = __ballot(mine);
-      const int before =
-          __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-      if (mine) dst[count + before] = p;
-      count += __popcll(m);
-    }
-  }
-  if (lane == 0) a.counts[id] = count;
-}
 
 // ---- Top-k selection of the indexer's scores (the positions a sparse decode
 // attends: "vllm-ascend PR #18870 解读：FlashComm1 的'假开启'与 SP 归位", §4.5,
@@ -1970,14 +1994,6 @@ hipError_t launch_decode(const DecodeArgs &args, int64_t grid, hipStream_t strea
     if (wide) hipLaunchKernelGGL((decode_kernel<kDenseStream, 128>), g, b, 0, stream, args);
     else hipLaunchKernelGGL((decode_kernel<kDenseStream, 64>), g, b, 0, stream, args);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_partition(const PartitionArgs &args, hipStream_t stream) {
-  const int64_t waves = (int64_t)args.B * args.lists_q * args.shard_units;
-  const int64_t per_block = kPartitionThreads / 64;
-  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)((waves + per_block - 1) / per_block)),
-                     dim3(kPartitionThreads), 0, stream, args);
   return hipGetLastError();
 }
 
