@@ -1620,30 +1620,34 @@ __global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWrite
 // reaches the number still to choose: after them the exact key T of the last
 // chosen element is known, and how many of the keys equal to T to take.  A last
 // pass marks the keys above T and the keys equal to T in two LDS bitmaps (a bit
-// per position); each thread takes two words of each, and one block-wide prefix
+// per position); each thread takes one word of each, and one block-wide prefix
 // sum of their counts gives every word its output offset (the chosen keys above
 // T before it, plus the ties before it up to the number taken).  The positions
 // are staged in LDS in order and written out coalesced.
 //
-// Layout: 512 threads; a segment of 32768 positions is 16 slabs of 2048, and
-// thread t holds positions 4t .. 4t+3 of every slab (one 16-byte load per
-// slab, coalesced across the wave), as keys in registers for all passes.
+// Layout: 1024 threads (16 waves, four per SIMD, so that the many short
+// LDS-bound steps of one row overlap); a segment of 32768 positions is 8 slabs
+// of 4096, and thread t holds positions 4t .. 4t+3 of every slab (one 16-byte
+// load per slab, coalesced across the wave), as keys in registers for all
+// passes.
 // Rows longer than one segment are taken segment by segment, reloaded per
 // pass.
 //
 // A wave's LDS atomic costs about the same however few of its lanes take
 // part, so the passes of a row that fits one segment work on short lists:
-// each thread's m-th largest key, m = ceil(k / 512), bounds T from below by
-// the smallest of them (at least 512 m >= k keys reach it); every wave copies
+// each thread's m-th largest key, m = ceil(k / 1024), bounds T from below by
+// the smallest of them (at least 1024 m >= k keys reach it); every wave copies
 // its keys at or above that bound into its own LDS list, counts the list, and
 // after each pass keeps only the keys that match the digits chosen so far.
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkSlabs = 16;                                 // slabs of 2048 positions per segment
+constexpr int kTopkSlabs = 8;                                  // slabs of 4096 positions per segment
 constexpr int kTopkSlabLen = 4 * kTopkThreads;
 constexpr int kTopkPerThread = 4 * kTopkSlabs;                 // keys held per thread
 constexpr int kTopkSeg = kTopkThreads * kTopkPerThread;        // 32768 positions per segment
 constexpr int kTopkMapWords = kTopkSeg / 32;                  // bitmap words per segment
+constexpr int kTopkMapPerThread = kTopkMapWords / kTopkThreads;  // words of each bitmap a thread takes
+static_assert(kTopkMapPerThread >= 1 && kTopkMapPerThread * kTopkThreads == kTopkMapWords, "bitmap split");
 constexpr int kTopkMaxM = 4;                                   // largest m the lower bound is formed for
 
 __device__ __forceinline__ uint32_t rank_key(float x) {
@@ -1745,17 +1749,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   uint32_t lo = 1u, hi = 0xffffffffu;
   const int m = (k + kTopkThreads - 1) / kTopkThreads;
   if (resident && m <= kTopkMaxM) {
-    uint32_t t[kTopkMaxM] = {0u, 0u, 0u, 0u};  // this thread's largest keys, descending
+    // This thread's m largest keys, descending (an insertion network m deep).
+    uint32_t t[kTopkMaxM] = {0u, 0u, 0u, 0u};
+    auto largest = [&](auto depth) {
+      constexpr int kDepth = decltype(depth)::value;
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j) {
-      uint32_t x = key[j];
+      for (int j = 0; j < kTopkPerThread; ++j) {
+        uint32_t x = key[j];
 #pragma unroll
-      for (int r = 0; r < kTopkMaxM; ++r) {
-        const uint32_t hi = max(t[r], x);
-        x = min(t[r], x);
-        t[r] = hi;
+        for (int r = 0; r < kDepth; ++r) {
+          const uint32_t hi = max(t[r], x);
+          x = min(t[r], x);
+          t[r] = hi;
+        }
       }
-    }
+    };
+    if (m == 1) largest(std::integral_constant<int, 1>());
+    else if (m == 2) largest(std::integral_constant<int, 2>());
+    else if (m == 3) largest(std::integral_constant<int, 3>());
+    else largest(std::integral_constant<int, 4>());
     const uint32_t mth = m == 1 ? t[0] : m == 2 ? t[1] : m == 3 ? t[2] : t[3];
     // threads with fewer than m keys (mth == 0) do not take part
     uint32_t mn = mth ? mth : 0xffffffffu, cnt = mth ? 1u : 0u, mx = t[0];
@@ -1810,8 +1822,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   }
 
   // Pass 1 over few top bytes: when the keys from lo to hi span at most 8
-  // top-byte values, per-lane counters and a wave sum replace the atomics
-  // (whose lanes would mostly hit the same few words).
+  // top-byte values, ballot counts replace the atomics (whose lanes would
+  // mostly hit the same few words).
   const uint32_t base8 = lo >> 24;
   const bool narrow = resident && (hi >> 24) - base8 < 8u;
 #pragma unroll
@@ -1821,16 +1833,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
     // hist[] is zero here (cleared where it was last summed)
     if (resident && pass == 0 && narrow) {
+      // Wave-wide counts by ballot, for the top-byte values the list can hold
+      // (span of them, at most 8; a chunk's keys past the list count nowhere).
+      const uint32_t span = (hi >> 24) - base8 + 1u;
       uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-      for (uint32_t i = lane; i < n; i += 64) {
-        const uint32_t d = (cand[wave][i] >> 24) - base8;
+      for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+        const uint32_t i = i0 + lane;
+        const uint32_t d = i < n ? (cand[wave][i] >> 24) - base8 : 8u;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) c[r] += d == (uint32_t)r;
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) c[r] += __shfl_xor(c[r], o, 64);
+        for (int r = 0; r < 8; ++r)
+          if ((uint32_t)r < span) c[r] += (uint32_t)__popcll(__ballot(d == (uint32_t)r));
       }
       if (lane < 8) {
         uint32_t v = c[0];
@@ -1918,15 +1930,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
       if (e) atomicOr(&eq_map[w], e << sh);
     }
     __syncthreads();
-    const int w0 = 2 * tid;
-    const uint32_t g0 = gt_map[w0], g1 = gt_map[w0 + 1], e0 = eq_map[w0], e1 = eq_map[w0 + 1];
+    const int w0 = kTopkMapPerThread * tid;
+    uint32_t gw[kTopkMapPerThread], ew[kTopkMapPerThread];
+    uint32_t cg = 0, ce = 0;
+#pragma unroll
+    for (int h = 0; h < kTopkMapPerThread; ++h) {
+      gw[h] = gt_map[w0 + h];
+      ew[h] = eq_map[w0 + h];
+      cg += __popc(gw[h]);
+      ce += __popc(ew[h]);
+    }
     uint32_t sums;
-    const uint32_t before = block_exclusive_sum((uint32_t)(__popc(g0) + __popc(g1)) |
-                                                    ((uint32_t)(__popc(e0) + __popc(e1)) << 16), part, sums);
+    const uint32_t before = block_exclusive_sum(cg | (ce << 16), part, sums);
     uint32_t above_before = above_seen + (before & 0xffffu), eq_before = equal_seen + (before >> 16);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t g = h ? g1 : g0, e = h ? e1 : e0;
+    for (int h = 0; h < kTopkMapPerThread; ++h) {
+      const uint32_t g = gw[h], e = ew[h];
       const uint32_t take = remaining > eq_before ? remaining - eq_before : 0u;
       uint32_t sel = g | lowest_bits(e, take);
       uint32_t o = above_before + min(eq_before, remaining);
