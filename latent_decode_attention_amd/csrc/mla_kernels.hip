@@ -680,6 +680,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // `between` runs after the positions and `after_blocks` after the block ids
   // are issued: the first pass loads the query rows there, so each wait of
   // the chain leaves the query loads issued after it in flight.
+  // `before_copy` runs once the rows are known, before the copy of tile 0 is
+  // issued (64-row groups stage their query halves in LDS there, so that the
+  // exchange of the halves overlaps the copy in flight instead of following
+  // it; any wait on a load placed after the copies would drain them too).
   TileMask mask_cur;
   int pn1, bn1, pn2;
   int row_cur = -1;  // 64-row groups: cache row of this lane's token (lane = token) in the current tile
@@ -687,7 +691,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // and whether its token is attended at all (else the factor is taken as 0).
   float sig_raw = 0.f;
   bool sig_ok = false;
-  auto start_pass = [&](auto between, auto after_blocks) {
+  auto start_pass = [&](auto between, auto after_blocks, auto before_copy) {
     int plane = lane;
     asm volatile("" : "+v"(plane));
     const int p0 = raw_position<kMode>(a, u, u.i0 + plane);
@@ -703,6 +707,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     __builtin_amdgcn_sched_barrier(0);
     const int row0 = token_row(a, u, u.i0 + plane, p0, b0);
     if constexpr (kRows == 64) row_cur = row0;
+    before_copy();
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (kKv8) {
       copy_all8(prepare_copy8(sm.tile[0], a, wave, lane, row0), std::make_integer_sequence<int, kCopySteps8>());
       sig_raw = a.kv_scale[max(row0, 0)];
@@ -729,7 +735,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         [&]() {
 #pragma unroll
           for (int st = kQkSteps / 2; st < kQkSteps; ++st) qr[st] = qp[2 * st + half];
-        });
+        },
+        []() {});
   } else {
     // The two waves of a row tile hold the same query rows: each loads half of
     // the k-steps (token half th: k-steps 18 th..18 th+17, chosen through the
@@ -740,6 +747,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     constexpr int kHalf = kQkSteps / 2;
     bf16x8 tq[kHalf];
     const bf16x8 *qsrc = qp + 2 * kHalf * th;
+    bf16x8 *q_sh = reinterpret_cast<bf16x8 *>(sm.tile[1]) + rh * kQkSteps * 64 + lane;
     start_pass(
         [&]() {
 #pragma unroll
@@ -748,12 +756,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         [&]() {
 #pragma unroll
           for (int j = kHalf / 2; j < kHalf; ++j) tq[j] = qsrc[2 * j + half];
-        });
-    bf16x8 *q_sh = reinterpret_cast<bf16x8 *>(sm.tile[1]) + rh * kQkSteps * 64 + lane;
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the query halves (and the copy of tile 0) have landed
+        },
+        [&]() {
+          // The halves (issued after the block ids, landing about with them)
+          // go to LDS before tile 0 is copied; the compiler's waits for them
+          // then cover no direct copy.
 #pragma unroll
-    for (int j = 0; j < kHalf; ++j) q_sh[(kHalf * th + j) * 64] = tq[j];
-    lds_barrier();
+          for (int j = 0; j < kHalf; ++j) q_sh[(kHalf * th + j) * 64] = tq[j];
+        });
+    lds_barrier();  // every wave's half is in LDS (tile 0 may still be in flight)
 #pragma unroll
     for (int st = 0; st < kQkSteps; ++st) qr[st] = q_sh[st * 64];
     // (The first tile's top barrier orders these reads before any copy into
@@ -1089,7 +1100,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // Redo the unit with every reference raised to the largest score seen.
     m_ref = m_all;
     first_pass = false;
-    start_pass([]() {}, []() {});
+    start_pass([]() {}, []() {}, []() {});
   }
 
   // ---- finalize.  Each wave's outputs cover all rows, so the rounded row
