@@ -96,7 +96,6 @@ constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unc
 
 static_assert(kTile == 16 * kWaves, "each wave copies 16 rows of a tile");
 static_assert(kWaves == 4, "four waves: four row tiles, or two row tiles x two token halves");
-constexpr int kKAhead = 3;  // K operand reads in flight ahead of the MFMA that uses them
 
 // Source of the bytes copied for tokens that no query row attends, so that a
 // tile never holds stale or poisoned rows and the copies need no per-lane branch.
@@ -611,6 +610,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   constexpr int kSubBlocks = kRows / 64;    // 32-token score blocks per wave per tile
   constexpr int kPvSteps = 16;               // (k-block, column tile) steps of P.V
   constexpr int kCopyFirst = 3;              // first step that copies (after its addresses are formed)
+  // K operand reads in flight ahead of the MFMA that uses them: deep enough for
+  // the LDS latency while the copies land (64-row bf16 kernels); the 128-row
+  // and int8 kernels have no registers to spare for more than three.
+  constexpr int kKAhead = kRows == 64 && !kKv8 ? 5 : 3;
   constexpr int kSteps = kKv8 ? kCopySteps8 : kCopySteps;  // copy instructions per wave per tile
   constexpr int kCopyEvery = (kSubBlocks * kQkSteps + kPvSteps - kCopyFirst) / kSteps;
   static_assert(kCopyFirst + kCopyEvery * (kSteps - 1) < kSubBlocks * kQkSteps + kPvSteps,
@@ -1036,7 +1039,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       // e = 4..7 (rows +8..11): the k order of P^T.  V operands are read
       // kVAhead steps ahead and each k-block's weights two steps before it.
       {
-        constexpr int kVAhead = kRows == 128 ? 1 : 2;  // 4 (128 rows) or 2 MFMAs per V operand
+        constexpr int kVAhead = kRows == 128 ? 1 : 3;  // 4 (128 rows) or 2 MFMAs per V operand
         i16x4 vr[kVAhead + 1][2];
         bf16x8 pr[2][kRowTiles];
         auto v_read = [&](int j, i16x4 *dst) {
