@@ -975,32 +975,64 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
             x[r] = ((msk >> bit) & 1ull) ? s[r] : -INFINITY;
           }
         }
-        float smax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, x[r]);
-        {
-          // The token of the lane's largest score in this block (register
-          // index from the tag): 64-row groups keep its cache row, fetched
-          // from the lane that holds it; 128-row groups (no register to spare
-          // in the tile loop) its stream index, looked up at the end.
-          const int rb = (int)(__builtin_bit_cast(unsigned, smax) & 15u);
-          const int tok_b = 32 * tok + 8 * (rb >> 2) + 4 * half + (rb & 3);
-          const int id_b = kRows == 128 ? t * kTile + tok_b : __shfl(row_cur, tok_b);
-          if (smax > best_x) {
-            best_x = smax;
-            best_row = id_b;
+        // 64-row groups: the block's bookkeeping (block_max) follows the weights.
+        bool late = false;
+        float smax_l = -INFINITY, smax_o = -INFINITY;  // the lane's and the row's other lane's block maxima
+        int id_b = -1;
+        // The lane's best token, the row maximum, the reference where this
+        // block sets it, and the headroom check (64-row groups).  The weights
+        // need only the reference, so wherever it is already fixed (after the
+        // first tile of the first pass) this runs after the weights are formed
+        // and written: the latency of the two cross-lane reads it uses is then
+        // spent on the exponentials instead of being waited out in front of them.
+        auto block_max = [&]() {
+          if constexpr (kRows == 64) {
+            if (smax_l > best_x) {
+              best_x = smax_l;
+              best_row = id_b;
+            }
+            const float smax = fmaxf(smax_l, smax_o) * a.scale_log2;
+            if (first_pass && t == 0) {
+              // The row's reference: the larger first-tile maximum of its two waves.
+              if (half == 0) sm.mx[wave][n] = smax;
+              lds_barrier();
+              m_ref = fmaxf(sm.mx[rh][n], sm.mx[rh + 2][n]);
+            }
+            overflow |= smax > m_ref + kHeadroomLog2;
           }
-        }
-        smax = fmaxf(smax, __shfl_xor(smax, 32)) * a.scale_log2;
+        };
         if constexpr (kRows == 128) {
+          float smax = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) smax = fmaxf(smax, x[r]);
+          {
+            // The token of the lane's largest score in this block (register
+            // index from the tag): its stream index, looked up at the end (no
+            // register to spare in the tile loop of 128-row groups).
+            const int rb = (int)(__builtin_bit_cast(unsigned, smax) & 15u);
+            const int tok_b = 32 * tok + 8 * (rb >> 2) + 4 * half + (rb & 3);
+            const int id_b = t * kTile + tok_b;
+            if (smax > best_x) {
+              best_x = smax;
+              best_row = id_b;
+            }
+          }
+          smax = fmaxf(smax, __shfl_xor(smax, 32)) * a.scale_log2;
           if (m_ref == -INFINITY) m_ref = smax;  // first scores of this row: acc is still 0
-        } else if (first_pass && t == 0) {
-          // The row's reference: the larger first-tile maximum of its two waves.
-          if (half == 0) sm.mx[wave][n] = smax;
-          lds_barrier();
-          m_ref = fmaxf(sm.mx[rh][n], sm.mx[rh + 2][n]);
+          overflow |= smax > m_ref + kHeadroomLog2;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) smax_l = fmaxf(smax_l, x[r]);
+          // The token of the lane's largest score in this block (register
+          // index from the tag): its cache row, fetched from the lane that
+          // holds it.  Both cross-lane reads are issued here.
+          const int rb = (int)(__builtin_bit_cast(unsigned, smax_l) & 15u);
+          const int tok_b = 32 * tok + 8 * (rb >> 2) + 4 * half + (rb & 3);
+          id_b = __shfl(row_cur, tok_b);
+          smax_o = __shfl_xor(smax_l, 32);
+          late = !(first_pass && t == 0);
+          if (!late) block_max();
         }
-        overflow |= smax > m_ref + kHeadroomLog2;
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -1029,6 +1061,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           // P^T operand of k-block 2 tok + k, row tile rh: lane (row n, half)
           // holds tokens 16 (2 tok + k) + 8 (e / 4) + 4 half + e % 4.
           sm.p[2 * tok + k][rh][lane] = __builtin_bit_cast(bf16x8, w);
+        }
+        if constexpr (kRows == 64) {
+          if (late) {
+            // (Opaque to the compiler, so that the use of the cross-lane
+            // reads, and the wait for them, is not hoisted above the
+            // exponentials into code both paths share.)
+            asm volatile("" : "+v"(smax_o), "+v"(id_b));
+            block_max();
+          }
         }
       }
       __syncthreads();  // every wave's weights for this tile are in LDS
