@@ -1669,31 +1669,30 @@ __global__ __launch_bounds__(kKvWriteThreads) void kv_write_kernel(const KvWrite
 // written in ascending order and the row is padded with -1.
 //
 // One work-group per row.  Each score maps to a 32-bit key whose unsigned order
-// is that ranking (positions break the remaining ties).  Four passes, one per
-// 8-bit digit from the top, histogram the digit among keys that match the
-// digits chosen so far and pick the digit at which the count from the top
-// reaches the number still to choose: after them the exact key T of the last
-// chosen element is known, and how many of the keys equal to T to take.  A last
-// pass marks the keys above T and the keys equal to T in two LDS bitmaps (a bit
-// per position); each thread takes one word of each, and one block-wide prefix
-// sum of their counts gives every word its output offset (the chosen keys above
-// T before it, plus the ties before it up to the number taken).  The positions
-// are staged in LDS in order and written out coalesced.
+// is that ranking (positions break the remaining ties).  The selection finds the
+// exact key T of the last chosen element and how many of the keys equal to T to
+// take; a last pass marks the keys above T and the keys equal to T in two LDS
+// bitmaps (a bit per position); each thread takes one word of each, and one
+// block-wide prefix sum of their counts gives every word its output offset (the
+// chosen keys above T before it, plus the ties before it up to the number
+// taken).  The positions are staged in LDS in order and written out coalesced.
 //
 // Layout: 1024 threads (16 waves, four per SIMD, so that the many short
 // LDS-bound steps of one row overlap); a segment of 32768 positions is 8 slabs
 // of 4096, and thread t holds positions 4t .. 4t+3 of every slab (one 16-byte
-// load per slab, coalesced across the wave), as keys in registers for all
-// passes.
-// Rows longer than one segment are taken segment by segment, reloaded per
-// pass.
+// load per slab, coalesced across the wave), as keys in registers.
 //
-// A wave's LDS atomic costs about the same however few of its lanes take
-// part, so the passes of a row that fits one segment work on short lists:
-// each thread's m-th largest key, m = ceil(k / 1024), bounds T from below by
-// the smallest of them (at least 1024 m >= k keys reach it); every wave copies
-// its keys at or above that bound into its own LDS list, counts the list, and
-// after each pass keeps only the keys that match the digits chosen so far.
+// A row of at most one segment (its keys stay in registers) finds T in two
+// passes of 16 bits over a histogram of 65536 bins kept as 16-bit counts, two
+// to an LDS word (a row has fewer than 65536 keys, so no count carries into its
+// neighbour): the first bins the keys by their top half and finds the bin at
+// which the count from the top reaches k; the second bins the keys of that bin
+// by their low half.  Both add straight from the registers, and only keys at or
+// above a lower bound of T take part: each thread's m-th largest key, m =
+// ceil(k / 1024), bounds T from below by the smallest of them (at least
+// 1024 m >= k keys reach it), which keeps most keys of a typical row out of the
+// LDS atomics.  Longer rows are taken segment by segment, reloaded per pass,
+// with four passes of one 8-bit digit each.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkSlabs = 8;                                  // slabs of 4096 positions per segment
@@ -1704,6 +1703,10 @@ constexpr int kTopkMapWords = kTopkSeg / 32;                  // bitmap words pe
 constexpr int kTopkMapPerThread = kTopkMapWords / kTopkThreads;  // words of each bitmap a thread takes
 static_assert(kTopkMapPerThread >= 1 && kTopkMapPerThread * kTopkThreads == kTopkMapWords, "bitmap split");
 constexpr int kTopkMaxM = 4;                                   // largest m the lower bound is formed for
+constexpr int kTopkBinWords = 65536 / 2;                       // 16-bit bins, two per LDS word
+static_assert(kTopkSeg < 65536, "a bin's count must fit 16 bits");
+static_assert(kTopkBinWords >= kTopkWaves * 256 && kTopkBinWords >= kTopkSeg,
+              "the histogram's LDS also holds the digit histograms and the staged positions");
 
 __device__ __forceinline__ uint32_t rank_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -1712,16 +1715,56 @@ __device__ __forceinline__ uint32_t rank_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The unsigned order of the scores for every value but NaN and -0 (which
+// need rank_key): the sign bit set for non-negative values, all bits flipped
+// for negative ones.  The mapping is its own inverse up to that choice.
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t order_key_inverse(uint32_t key) {
+  return key ^ ((key & 0x80000000u) ? 0x80000000u : 0xffffffffu);
+}
+// NaN (either kind) or -0: the scores order_key ranks wrongly.
+__device__ __forceinline__ bool needs_rank_key(float x) { return __builtin_amdgcn_classf(x, 0x23); }
+
+// One step of a wave-wide scan through the DPP lane network: lanes that the
+// step's source pattern does not reach keep `id`.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_take(uint32_t x, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, kCtrl, kRowMask, 0xf, false);
+}
+// Inclusive scan over the 64 lanes of a wave, in registers: shifts by 1, 2, 4
+// and 8 lanes inside each row of 16, then the last lane of rows 0 and 2 into
+// rows 1 and 3, then the last lane of row 1 into rows 2 and 3.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_take<0x111, 0xf>(x, id));  // row_shr:1
+  x = op(x, dpp_take<0x112, 0xf>(x, id));  // row_shr:2
+  x = op(x, dpp_take<0x114, 0xf>(x, id));  // row_shr:4
+  x = op(x, dpp_take<0x118, 0xf>(x, id));  // row_shr:8
+  x = op(x, dpp_take<0x142, 0xa>(x, id));  // row_bcast:15
+  x = op(x, dpp_take<0x143, 0xc>(x, id));  // row_bcast:31
+  return x;
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, uint32_t id, Op op) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(x, id, op), 63);
+}
+struct AddU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MinU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+
 // Exclusive prefix sum over the work-group; `total` receives the sum.  The
 // trailing barrier frees `part`.
 __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *part, uint32_t &total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v, 0u, AddU32());
   if (lane == 63) part[wave] = x;
   __syncthreads();
   uint32_t base = 0, sum = 0;
@@ -1745,14 +1788,80 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t x, uint32_t n) {
   }
   return r;
 }
+// The packed histogram of 16-bit bins: bin b is the low (b even) or high half
+// of word b / 2.
+__device__ __forceinline__ uint32_t bin_count(const uint32_t *h, uint32_t b) {
+  return (h[b >> 1] >> ((b & 1u) << 4)) & 0xffffu;
+}
+__device__ __forceinline__ void bin_add(uint32_t *h, uint32_t b) { atomicAdd(&h[b >> 1], 1u << ((b & 1u) << 4)); }
+// Over the bins wlo .. whi of the packed histogram, the bin at which the count
+// from the top first reaches `need` (at least 1 and at most the window's total)
+// and the count of the bins above it.  The window is cut into runs of bins from
+// the top down; the count above each run comes from a prefix sum over the runs,
+// and the run that holds the crossing is walked by one wave, a bin per lane.
+// `res` [0, 1] receive the result ([4, 5] are scratch); every thread reads it
+// after the last barrier.
+__device__ __forceinline__ void crossing_bin(const uint32_t *h, uint32_t wlo, uint32_t whi, uint32_t need,
+                                             uint32_t *part, uint32_t *res, uint32_t &bin, uint32_t &above) {
+  const uint32_t span = whi > wlo ? whi - wlo : 0u, lane = threadIdx.x & 63;
+  // The crossing run (its top bin and the count above it), then the walk.
+  auto walk = [&](int64_t run_top, uint32_t per, uint32_t acc0) {
+    const int64_t b = run_top - (int64_t)lane;
+    const uint32_t c = lane < per && b >= (int64_t)wlo ? bin_count(h, (uint32_t)b) : 0u;
+    const uint32_t incl = wave_inclusive_scan(c, 0u, AddU32());
+    const unsigned long long hit = __ballot(acc0 + incl >= need);  // lanes at or past the crossing
+    if (lane == (uint32_t)(__ffsll((long long)hit) - 1)) {
+      res[0] = (uint32_t)b;
+      res[1] = acc0 + incl - c;
+    }
+  };
+  if (span < 64 * 64) {
+    // At most 4096 bins: wave 0 alone, runs of at most 64 bins, one per lane.
+    if (threadIdx.x < 64) {
+      const uint32_t per = span / 64 + 1;
+      const int64_t top = (int64_t)whi - (int64_t)lane * per;
+      uint32_t s = 0;
+      for (uint32_t i = 0; i < per; ++i) {
+        const int64_t b = top - i;
+        if (b >= (int64_t)wlo) s += bin_count(h, (uint32_t)b);
+      }
+      const uint32_t incl = wave_inclusive_scan(s, 0u, AddU32()), before = incl - s;
+      const unsigned long long hit = __ballot(before < need && need <= incl);
+      const uint32_t src = (uint32_t)(__ffsll((long long)hit) - 1);  // the lane whose run holds it
+      walk((int64_t)whi - (int64_t)src * per, per, (uint32_t)__builtin_amdgcn_readlane((int)before, (int)src));
+    }
+  } else {
+    // Runs of at most 64 bins, one per thread; the crossing run is handed to wave 0.
+    const uint32_t per = span / kTopkThreads + 1;
+    const int64_t top = (int64_t)whi - (int64_t)threadIdx.x * per;
+    uint32_t s = 0;
+    for (uint32_t i = 0; i < per; ++i) {
+      const int64_t b = top - i;
+      if (b >= (int64_t)wlo) s += bin_count(h, (uint32_t)b);
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_sum(s, part, total);
+    if (before < need && need <= before + s) {
+      res[4] = threadIdx.x;
+      res[5] = before;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) walk((int64_t)whi - (int64_t)res[4] * per, per, res[5]);
+  }
+  __syncthreads();
+  bin = res[0];
+  above = res[1];
+}
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
-  __shared__ uint32_t hist[kTopkWaves][256];
-  __shared__ uint32_t cand[kTopkWaves][64 * kTopkPerThread];  // each wave's candidate keys
+  // the packed 16-bit histogram; also the per-wave digit histograms of long
+  // rows, and the staged positions once T is known
+  __shared__ __attribute__((aligned(16))) uint32_t h32[kTopkBinWords];
   __shared__ uint32_t gt_map[kTopkMapWords], eq_map[kTopkMapWords];
   __shared__ uint32_t total[256];
   __shared__ uint32_t part[kTopkWaves];
   __shared__ uint32_t pick[2][2];  // per pass parity: chosen digit, count of keys above it
+  __shared__ uint32_t res[6];      // crossing bin and count above it; low-half min and max; scratch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   const int b = row / a.Q, q = row % a.Q;
@@ -1774,19 +1883,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (L & 3) == 0;
   const bool resident = L <= kTopkSeg;
   uint32_t key[kTopkPerThread];
+  // Keys come from order_key; a lane that loaded a NaN or a -0 redoes its keys
+  // with rank_key (rare, so the common path skips it).
   auto load = [&](int seg) {
+    bool special = false;
     if (vec) {
-      float4 f[kTopkSlabs];
+      u32x4 f[kTopkSlabs];
 #pragma unroll
       for (int j = 0; j < kTopkSlabs; ++j)
-        f[j] = *reinterpret_cast<const float4 *>(src + min(seg + kTopkSlabLen * j + 4 * tid, L - 4));
+        f[j] = *reinterpret_cast<const u32x4 *>(src + min(seg + kTopkSlabLen * j + 4 * tid, L - 4));
 #pragma unroll
       for (int j = 0; j < kTopkSlabs; ++j) {
-        const bool in = seg + kTopkSlabLen * j + 4 * tid < L;  // all four or none
-        key[4 * j] = in ? rank_key(f[j].x) : 0u;
-        key[4 * j + 1] = in ? rank_key(f[j].y) : 0u;
-        key[4 * j + 2] = in ? rank_key(f[j].z) : 0u;
-        key[4 * j + 3] = in ? rank_key(f[j].w) : 0u;
+        // keeps the compiler from merging this branch into the 4-byte one
+        // (whose key arithmetic is the same) and splitting the 16-byte loads
+        asm volatile("" : "+v"(f[j]));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          key[4 * j + c] = order_key(f[j][c]);
+          special |= needs_rank_key(__uint_as_float(f[j][c]));
+        }
       }
     } else {
       float f[kTopkPerThread];
@@ -1794,11 +1909,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
       for (int j = 0; j < kTopkPerThread; ++j)
         f[j] = src[min(seg + kTopkSlabLen * (j >> 2) + 4 * tid + (j & 3), L - 1)];
 #pragma unroll
+      for (int j = 0; j < kTopkPerThread; ++j) {
+        key[j] = order_key(__float_as_uint(f[j]));
+        special |= needs_rank_key(f[j]);
+      }
+    }
+    if (special) {
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread; ++j) key[j] = rank_key(__uint_as_float(order_key_inverse(key[j])));
+    }
+    if (seg + kTopkSeg > L) {  // the row ends in this segment: key 0 past it
+      const int rem = L - seg - 4 * tid;  // this thread's key j is in the row iff its offset is below rem
+#pragma unroll
       for (int j = 0; j < kTopkPerThread; ++j)
-        key[j] = seg + kTopkSlabLen * (j >> 2) + 4 * tid + (j & 3) < L ? rank_key(f[j]) : 0u;
+        key[j] = kTopkSlabLen * (j >> 2) + (j & 3) < rem ? key[j] : 0u;
     }
   };
-  if (resident) load(0);
+  if (resident) {
+    // clear the histogram (its words are first used after the lower bound's
+    // barrier), then load the row
+#pragma unroll
+    for (int i = 0; i < kTopkBinWords / 4 / kTopkThreads; ++i)
+      reinterpret_cast<u32x4 *>(h32)[tid + i * kTopkThreads] = u32x4{0u, 0u, 0u, 0u};
+    load(0);
+  }
 
   // Lower bound of T (keys below it are never counted) and the largest key.
   uint32_t lo = 1u, hi = 0xffffffffu;
@@ -1811,11 +1945,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
 #pragma unroll
       for (int j = 0; j < kTopkPerThread; ++j) {
         uint32_t x = key[j];
+        if constexpr (kDepth == 2) {  // t0 >= t1: the new second largest is the median
+          t[1] = max(t[1], min(t[0], x));
+          t[0] = max(t[0], x);
+        } else {
 #pragma unroll
-        for (int r = 0; r < kDepth; ++r) {
-          const uint32_t hi = max(t[r], x);
-          x = min(t[r], x);
-          t[r] = hi;
+          for (int r = 0; r < kDepth; ++r) {
+            const uint32_t hi = max(t[r], x);
+            x = min(t[r], x);
+            t[r] = hi;
+          }
         }
       }
     };
@@ -1825,13 +1964,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
     else largest(std::integral_constant<int, 4>());
     const uint32_t mth = m == 1 ? t[0] : m == 2 ? t[1] : m == 3 ? t[2] : t[3];
     // threads with fewer than m keys (mth == 0) do not take part
-    uint32_t mn = mth ? mth : 0xffffffffu, cnt = mth ? 1u : 0u, mx = t[0];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      mn = min(mn, (uint32_t)__shfl_xor(mn, o, 64));
-      mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
-      cnt += __shfl_xor(cnt, o, 64);
-    }
+    const uint32_t mn = wave_reduce(mth ? mth : 0xffffffffu, 0xffffffffu, MinU32());
+    const uint32_t cnt = wave_reduce(mth ? 1u : 0u, 0u, AddU32());
+    const uint32_t mx = wave_reduce(t[0], 0u, MaxU32());
     if (lane == 0) {
       total[wave] = mn;
       total[kTopkWaves + wave] = cnt;
@@ -1850,64 +1985,53 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
     hi = bmax;
   }
 
-  // This wave's list: its keys >= lo (resident rows only), in any order.
-  uint32_t n = 0;  // wave-uniform length
-  auto keep_list = [&](auto keep) {  // in place: a chunk is read before any write reaches it
-    uint32_t m2 = 0;
-    for (uint32_t base = 0; base < n; base += 64) {
-      const uint32_t i = base + lane;
-      const uint32_t kk = cand[wave][min(i, n - 1)];
-      const bool in = i < n && keep(kk);
-      const unsigned long long bm = __ballot(in);
-      if (in)
-        cand[wave][m2 + __builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, 0u))] = kk;
-      m2 += __popcll(bm);
-    }
-    n = m2;
-  };
+  uint32_t prefix = 0, remaining = (uint32_t)k;
   if (resident) {
+    if (m > kTopkMaxM) __syncthreads();  // the cleared histogram (else the lower bound's barriers order it)
+    // Top halves of the keys at or above lo: the bin of T and the count above it.
+#pragma unroll
+    for (int j = 0; j < kTopkPerThread; ++j)
+      if (key[j] >= lo) bin_add(h32, key[j] >> 16);
+    __syncthreads();
+    uint32_t b1, above1;
+    crossing_bin(h32, lo >> 16, hi >> 16, (uint32_t)k, part, res, b1, above1);
+    // Only the bins lo .. hi were counted into: clear their words again.
+    for (uint32_t w = (lo >> 17) + (uint32_t)tid; w <= (hi >> 17); w += kTopkThreads) h32[w] = 0u;
+    if (tid == 0) {
+      res[2] = 0xffffu;
+      res[3] = 0u;
+    }
+    __syncthreads();
+    // Low halves of the counted keys in that bin, and their range.
 #pragma unroll
     for (int j = 0; j < kTopkPerThread; ++j) {
-      const bool in = key[j] >= lo;
-      const unsigned long long bm = __ballot(in);
-      if (in)
-        cand[wave][n + __builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, 0u))] = key[j];
-      n += __popcll(bm);
+      const uint32_t kk = key[j];
+      if (kk >= lo && (kk >> 16) == b1) {
+        const uint32_t l = kk & 0xffffu;
+        bin_add(h32, l);
+        // a per-lane address: plain LDS atomics rather than a wave-wide
+        // reduction loop in each of the 32 unrolled copies
+        uint32_t z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        atomicMin(&res[2] + z, l);
+        atomicMax(&res[3] + z, l);
+      }
     }
-  }
-
-  // Pass 1 over few top bytes: when the keys from lo to hi span at most 8
-  // top-byte values, ballot counts replace the atomics (whose lanes would
-  // mostly hit the same few words).
-  const uint32_t base8 = lo >> 24;
-  const bool narrow = resident && (hi >> 24) - base8 < 8u;
+    __syncthreads();
+    uint32_t b2, above2;
+    crossing_bin(h32, res[2], res[3], (uint32_t)k - above1, part, res, b2, above2);
+    prefix = (b1 << 16) | b2;
+    remaining = (uint32_t)k - above1 - above2;
+  } else {
+    // Four 8-bit digits from the top, each histogrammed per wave over the keys
+    // that match the digits chosen so far.
+    uint32_t(*hist)[256] = reinterpret_cast<uint32_t(*)[256]>(h32);
 #pragma unroll
-  for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) (&hist[0][0])[tid + i * kTopkThreads] = 0u;
-  __syncthreads();
-  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
-  for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
-    // hist[] is zero here (cleared where it was last summed)
-    if (resident && pass == 0 && narrow) {
-      // Wave-wide counts by ballot, for the top-byte values the list can hold
-      // (span of them, at most 8; a chunk's keys past the list count nowhere).
-      const uint32_t span = (hi >> 24) - base8 + 1u;
-      uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-      for (uint32_t i0 = 0; i0 < n; i0 += 64) {
-        const uint32_t i = i0 + lane;
-        const uint32_t d = i < n ? (cand[wave][i] >> 24) - base8 : 8u;
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          if ((uint32_t)r < span) c[r] += (uint32_t)__popcll(__ballot(d == (uint32_t)r));
-      }
-      if (lane < 8) {
-        uint32_t v = c[0];
-#pragma unroll
-        for (int r = 1; r < 8; ++r) v = lane == r ? c[r] : v;
-        if (base8 + lane < 256u) hist[wave][base8 + lane] = v;
-      }
-    } else if (resident) {
-      for (uint32_t i = lane; i < n; i += 64) atomicAdd(&hist[wave][(cand[wave][i] >> shift) & 255u], 1u);
-    } else {
+    for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) (&hist[0][0])[tid + i * kTopkThreads] = 0u;
+    __syncthreads();
+    uint32_t mask = 0;
+    for (int shift = 24, pass = 0; shift >= 0; shift -= 8, ++pass) {
+      // hist[] is zero here (cleared where it was last summed)
       for (int seg = 0; seg < L; seg += kTopkSeg) {
         load(seg);
 #pragma unroll
@@ -1916,53 +2040,52 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
           if (kk != 0u && (kk & mask) == prefix) atomicAdd(&hist[wave][(kk >> shift) & 255u], 1u);
         }
       }
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t t = 0;
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t t = 0;
 #pragma unroll
-      for (int c = 0; c < kTopkWaves; ++c) {
-        t += hist[c][tid];
-        hist[c][tid] = 0u;
-      }
-      total[tid] = t;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // Lane l owns digits 4l .. 4l+3.  Count above its digits = the sum over
-      // higher lanes; then walk its own digits downwards.
-      uint32_t c[4], own = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = total[4 * lane + j];
-        own += c[j];
-      }
-      uint32_t x = own;  // inclusive sum from the top lane down
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(x, o, 64);
-        if (lane + o < 64) x += y;
-      }
-      uint32_t above = x - own;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < remaining && remaining <= above + c[j]) {
-          pick[pass & 1][0] = (uint32_t)(4 * lane + j);
-          pick[pass & 1][1] = above;
+        for (int c = 0; c < kTopkWaves; ++c) {
+          t += hist[c][tid];
+          hist[c][tid] = 0u;
         }
-        above += c[j];
+        total[tid] = t;
       }
+      __syncthreads();
+      if (wave == 0) {
+        // Lane l owns digits 4l .. 4l+3.  Count above its digits = the sum over
+        // higher lanes; then walk its own digits downwards.
+        uint32_t c[4], own = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = total[4 * lane + j];
+          own += c[j];
+        }
+        uint32_t x = own;  // inclusive sum from the top lane down
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_down(x, o, 64);
+          if (lane + o < 64) x += y;
+        }
+        uint32_t above = x - own;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (above < remaining && remaining <= above + c[j]) {
+            pick[pass & 1][0] = (uint32_t)(4 * lane + j);
+            pick[pass & 1][1] = above;
+          }
+          above += c[j];
+        }
+      }
+      __syncthreads();
+      prefix |= pick[pass & 1][0] << shift;
+      mask |= 255u << shift;
+      remaining -= pick[pass & 1][1];
     }
-    __syncthreads();
-    prefix |= pick[pass & 1][0] << shift;
-    mask |= 255u << shift;
-    remaining -= pick[pass & 1][1];
-    if (resident && shift > 0) keep_list([&](uint32_t kk) { return (kk & mask) == prefix; });
   }
   // prefix is now the key T of the last element chosen; `remaining` of the keys
   // equal to T are taken, lowest positions first.
   const bool staged = k <= kTopkSeg;  // positions staged in LDS (the lists are done)
-  uint32_t *stage = &cand[0][0];
+  uint32_t *stage = h32;
   uint32_t above_seen = 0, equal_seen = 0;
   for (int seg = 0; seg < L; seg += kTopkSeg) {
     if (!resident) load(seg);
