@@ -1885,6 +1885,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
   uint32_t key[kTopkPerThread];
   // Keys come from order_key; a lane that loaded a NaN or a -0 redoes its keys
   // with rank_key (rare, so the common path skips it).
+  uint32_t low_or = 0;  // the loaded scores' low 16 bits, OR-ed (nonzero also after a NaN or -0)
   auto load = [&](int seg) {
     bool special = false;
     if (vec) {
@@ -1901,6 +1902,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
         for (int c = 0; c < 4; ++c) {
           key[4 * j + c] = order_key(f[j][c]);
           special |= needs_rank_key(__uint_as_float(f[j][c]));
+          low_or |= f[j][c] & 0xffffu;
         }
       }
     } else {
@@ -1912,9 +1914,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
       for (int j = 0; j < kTopkPerThread; ++j) {
         key[j] = order_key(__float_as_uint(f[j]));
         special |= needs_rank_key(f[j]);
+        low_or |= __float_as_uint(f[j]) & 0xffffu;
       }
     }
     if (special) {
+      low_or = 1u;
 #pragma unroll
       for (int j = 0; j < kTopkPerThread; ++j) key[j] = rank_key(__uint_as_float(order_key_inverse(key[j])));
     }
@@ -1936,6 +1940,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
 
   // Lower bound of T (keys below it are never counted) and the largest key.
   uint32_t lo = 1u, hi = 0xffffffffu;
+  bool wide_keys = true;  // some score of the row has nonzero low 16 bits (or is NaN / -0)
   const int m = (k + kTopkThreads - 1) / kTopkThreads;
   if (resident && m <= kTopkMaxM) {
     // This thread's m largest keys, descending (an insertion network m deep).
@@ -1967,19 +1972,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
     const uint32_t mn = wave_reduce(mth ? mth : 0xffffffffu, 0xffffffffu, MinU32());
     const uint32_t cnt = wave_reduce(mth ? 1u : 0u, 0u, AddU32());
     const uint32_t mx = wave_reduce(t[0], 0u, MaxU32());
+    const uint32_t wl = wave_reduce(low_or, 0u, [](uint32_t x, uint32_t y) { return x | y; });
     if (lane == 0) {
       total[wave] = mn;
       total[kTopkWaves + wave] = cnt;
       total[2 * kTopkWaves + wave] = mx;
+      total[3 * kTopkWaves + wave] = wl;
     }
     __syncthreads();
-    uint32_t bmin = 0xffffffffu, bcnt = 0, bmax = 0;
+    // The scheduling fences at the phase boundaries of this kernel keep the
+    // compiler from moving work across them (measured: without them a call
+    // takes about 2 us longer).
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t bmin = 0xffffffffu, bcnt = 0, bmax = 0, bl = 0;
 #pragma unroll
     for (int i = 0; i < kTopkWaves; ++i) {
       bmin = min(bmin, total[i]);
       bcnt += total[kTopkWaves + i];
       bmax = max(bmax, total[2 * kTopkWaves + i]);
+      bl |= total[3 * kTopkWaves + i];
     }
+    wide_keys = bl != 0;
     __syncthreads();
     if (bcnt * (uint32_t)m >= (uint32_t)k) lo = bmin;
     hi = bmax;
@@ -1993,35 +2006,48 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
     for (int j = 0; j < kTopkPerThread; ++j)
       if (key[j] >= lo) bin_add(h32, key[j] >> 16);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t b1, above1;
     crossing_bin(h32, lo >> 16, hi >> 16, (uint32_t)k, part, res, b1, above1);
-    // Only the bins lo .. hi were counted into: clear their words again.
-    for (uint32_t w = (lo >> 17) + (uint32_t)tid; w <= (hi >> 17); w += kTopkThreads) h32[w] = 0u;
-    if (tid == 0) {
-      res[2] = 0xffffu;
-      res[3] = 0u;
-    }
-    __syncthreads();
-    // Low halves of the counted keys in that bin, and their range.
-#pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j) {
-      const uint32_t kk = key[j];
-      if (kk >= lo && (kk >> 16) == b1) {
-        const uint32_t l = kk & 0xffffu;
-        bin_add(h32, l);
-        // a per-lane address: plain LDS atomics rather than a wave-wide
-        // reduction loop in each of the 32 unrolled copies
-        uint32_t z;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-        atomicMin(&res[2] + z, l);
-        atomicMax(&res[3] + z, l);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!wide_keys) {
+      // Every score is a bf16 value: all keys of a bin are equal (low half 0
+      // for non-negative scores, all ones for negative ones), so the bin
+      // gives T.
+      prefix = (b1 << 16) | ((b1 & 0x8000u) ? 0u : 0xffffu);
+      remaining = (uint32_t)k - above1;
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // Only the bins lo .. hi were counted into: clear their words again.
+      for (uint32_t w = (lo >> 17) + (uint32_t)tid; w <= (hi >> 17); w += kTopkThreads) h32[w] = 0u;
+      if (tid == 0) {
+        res[2] = 0xffffu;
+        res[3] = 0u;
       }
+      __syncthreads();
+      // Low halves of the counted keys in that bin, and their range.
+#pragma unroll
+      for (int j = 0; j < kTopkPerThread; ++j) {
+        const uint32_t kk = key[j];
+        if (kk >= lo && (kk >> 16) == b1) {
+          const uint32_t l = kk & 0xffffu;
+          bin_add(h32, l);
+          // a per-lane address: plain LDS atomics rather than a wave-wide
+          // reduction loop in each of the 32 unrolled copies
+          uint32_t z;
+          asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+          atomicMin(&res[2] + z, l);
+          atomicMax(&res[3] + z, l);
+        }
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t b2, above2;
+      crossing_bin(h32, res[2], res[3], (uint32_t)k - above1, part, res, b2, above2);
+      prefix = (b1 << 16) | b2;
+      remaining = (uint32_t)k - above1 - above2;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    uint32_t b2, above2;
-    crossing_bin(h32, res[2], res[3], (uint32_t)k - above1, part, res, b2, above2);
-    prefix = (b1 << 16) | b2;
-    remaining = (uint32_t)k - above1 - above2;
   } else {
     // Four 8-bit digits from the top, each histogrammed per wave over the keys
     // that match the digits chosen so far.
@@ -2108,6 +2134,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
       if (e) atomicOr(&eq_map[w], e << sh);
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     const int w0 = kTopkMapPerThread * tid;
     uint32_t gw[kTopkMapPerThread], ew[kTopkMapPerThread];
     uint32_t cg = 0, ce = 0;
@@ -2140,10 +2167,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs a) {
       above_before += __popc(g);
       eq_before += __popc(e);
     }
+    __builtin_amdgcn_sched_barrier(0);
     above_seen += sums & 0xffffu;
     equal_seen += sums >> 16;
     __syncthreads();  // the bitmaps are cleared for the next segment
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (staged)
     for (int i = tid; i < k; i += kTopkThreads) dst[i] = stage[i];
 }

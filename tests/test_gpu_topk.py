@@ -91,3 +91,16 @@ def test_topk_of_unaligned_strided_rows():
     got = md.mla_topk_select(s, torch.from_numpy(x.seq_lens).cuda(), 1000)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), topk.select(x.scores, x.seq_lens, 1000))
+
+
+@pytest.mark.parametrize("B,lens,k", [(4, [32768, 30000, 5000, 2049], 2048), (2, [32768, 9000], 300),
+                                      (32, [32768] * 32, 2048)])
+def test_topk_of_full_precision_scores(B, lens, k):
+    # fp32 scores using all 32 bits (the other cases hold bf16 values): the
+    # low halves of the keys decide the last chosen score, and the zeros and
+    # the +inf past each row are kept
+    x = W.make_topk_scores(B, 1, lens, k, seed=31 + B)
+    full = np.random.default_rng(33 + B).standard_normal(x.scores.shape).astype(np.float32)
+    x.scores[...] = np.where(np.isinf(x.scores) | (x.scores == 0), x.scores, full)
+    assert (x.scores.view(np.uint32) & 0xffff).any()
+    assert np.array_equal(gpu_select(x), topk.select(x.scores, x.seq_lens, k))
