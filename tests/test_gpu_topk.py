@@ -29,6 +29,8 @@ def gpu_select(x, top_k=None):
 @pytest.mark.parametrize("B,Q,lens,k", [
     (1, 1, [1], 1), (1, 1, [5], 8), (2, 1, [3000, 1024], 1024), (3, 2, [5000, 100, 2049], 2048),
     (4, 4, [70, 4097, 1, 2052], 2048), (2, 1, [131072, 99999], 2048), (2, 3, [40000, 3], 1), (1, 1, [65536], 65536),
+    # rows of one segment with k > 4096: no per-thread lower bound, every key counted
+    (1, 1, [32768], 20000), (2, 1, [30000, 9000], 5000), (1, 2, [32768], 32766),
 ])
 def test_topk_matches_the_oracle(B, Q, lens, k):
     x = W.make_topk_scores(B, Q, lens, k, seed=B * 100 + Q + k)
@@ -94,7 +96,7 @@ def test_topk_of_unaligned_strided_rows():
 
 
 @pytest.mark.parametrize("B,lens,k", [(4, [32768, 30000, 5000, 2049], 2048), (2, [32768, 9000], 300),
-                                      (32, [32768] * 32, 2048)])
+                                      (32, [32768] * 32, 2048), (2, [32767, 20001], 6000)])
 def test_topk_of_full_precision_scores(B, lens, k):
     # fp32 scores using all 32 bits (the other cases hold bf16 values): the
     # low halves of the keys decide the last chosen score, and the zeros and
